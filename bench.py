@@ -1,0 +1,166 @@
+"""Benchmark: routed-MoE layer forward on one MI355X.
+
+A step is one moe_layer_forward call (router GEMM, softmax top-k, permute,
+grouped SwiGLU FFN, combine) over the whole workload, with every input already
+resident in HBM.  The default workload is the page's layer shape (hidden 6,144,
+384 routed experts, top-8, expert hidden 1,792, bf16) on one 65,536-token
+sequence with Zipf-like routing skew.
+
+Prints one JSON line.  `roofline` covers the grouped FFN (its gate/up and down
+GEMM launches, timed together with HIP events on the launch stream) against
+the bf16 dense MFMA peak; `stages_ms` gives each step's average duration from
+a second, stage-by-stage pass; `cpu_baseline` times the float64 CPU oracle on a
+bounded slice of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer fwd tokens/s + grouped-GEMM % bf16 MFMA peak (d6144,E384,top8)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="page_seq64k_skewed")
+    ap.add_argument("--cpu-tokens", type=int, default=512,
+                    help="tokens of the workload the CPU oracle runs on (0 = skip)")
+    return ap.parse_args()
+
+
+def stage_pass(torch, B, inp, wl, steps):
+    """Average per-stage durations (ms) with events on the current stream."""
+    routed = inp["w_router"] is not None
+    names = (["route"] if routed else []) + ["permute", "grouped_ffn", "combine"]
+    acc = {n: 0.0 for n in names}
+    for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        ev[0].record()
+        i = 0
+        if routed:
+            ids, w, _ = B.moe_route(inp["x"], inp["w_router"], wl.k, bias=inp["bias"], want_logits=False)
+            i += 1
+            ev[i].record()
+        else:
+            ids, w = inp["topk_ids"], inp["topk_w"]
+        off, rt, sr, xp = B.moe_permute(inp["x"], ids, wl.E)
+        i += 1
+        ev[i].record()
+        yp = B.moe_grouped_ffn(xp, off, inp["w_gate"], inp["w_up"], inp["w_down"], y_perm=xp)
+        i += 1
+        ev[i].record()
+        B.moe_combine(yp, sr, w)
+        i += 1
+        ev[i].record()
+        torch.cuda.synchronize()
+        for j, n in enumerate(names):
+            acc[n] += ev[j].elapsed_time(ev[j + 1])
+        del off, rt, sr, xp, yp
+    return {n: v / steps for n, v in acc.items()}
+
+
+def cpu_baseline(torch, inp, wl, n_tokens):
+    """The float64 oracle on the first n_tokens tokens of the workload (their
+    routing, permutation, every expert FFN they use, and the combine)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import moe_oracle as orc
+
+    f64 = lambda t: None if t is None else t.detach().to("cpu").to(torch.float64).numpy()
+    n = min(n_tokens, wl.T)
+    x = f64(inp["x"][:n])
+    routed = inp["w_router"] is not None
+    host = {k: inp[k].cpu() for k in ("w_gate", "w_up", "w_down")}   # bf16 on the host, as stored
+    to_np = lambda t: (t.view(torch.int16).numpy().view(np.uint16))  # bf16 bits; the oracle widens them
+    wg = [to_np(host["w_gate"][e]) for e in range(wl.E)]
+    wu = [to_np(host["w_up"][e]) for e in range(wl.E)]
+    wd = [to_np(host["w_down"][e]) for e in range(wl.E)]
+    kw = {}
+    if not routed:
+        kw = dict(ids=inp["topk_ids"][:n].cpu().numpy(), weights=inp["topk_w"][:n].cpu().numpy())
+    wr, b = f64(inp["w_router"]), f64(inp["bias"])
+    t0 = time.perf_counter()
+    orc.layer_forward(x, wr, b, wg, wu, wd, wl.k, **kw)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {wl.T} tokens of {wl.name}: float64 oracle end to end (routing, "
+                      f"permutation, SwiGLU FFN of every expert they use, combine); {dt:.1f} s on "
+                      f"{threads} BLAS threads of {os.cpu_count()} host CPUs"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the layer's expert-parallel sharding is described in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixture_experts_layer_16_amd import binding as B
+    from mixture_experts_layer_16_amd import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    inp = W.make_inputs(wl, device="cuda:0")
+    L = B.LayerForward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"], inp["w_down"], wl.k,
+                       topk_ids=inp.get("topk_ids"), topk_w=inp.get("topk_w"))
+    for _ in range(args.warmup):
+        L()
+    torch.cuda.synchronize()
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        L()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    tokens_per_s = wl.T / (ms / 1e3)
+
+    stages = stage_pass(torch, B, inp, wl, max(2, min(args.steps, 5)))
+    ffn_ms = stages["grouped_ffn"]
+    peak = PEAK_BF16_TFLOPS if wl.dtype == torch.bfloat16 else PEAK_F32_TFLOPS
+    ffn_tflops = wl.expert_flops() / (ffn_ms / 1e3) / 1e12
+    total_tflops = (wl.expert_flops() + wl.router_flops()) / (ms / 1e3) / 1e12
+    es = 2 if wl.dtype == torch.bfloat16 else 4
+    perm_bytes = wl.T * wl.d * es + wl.N * wl.d * es + wl.T * wl.k * 4 * 3
+    comb_bytes = wl.N * wl.d * es + wl.T * wl.d * es + wl.T * wl.k * 8
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded random inputs and weights of the page's layer shape)",
+        "config": {"workload": wl.name, "tokens": wl.T, "hidden": wl.d, "experts": wl.E, "top_k": wl.k,
+                   "expert_hidden": wl.F, "routing": wl.routing, "slots": wl.N},
+        "roofline": {"bound": "mfma", "achieved": round(ffn_tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(ffn_tflops / peak, 4), "traffic": None,
+                     "kernel": "grouped SwiGLU FFN (gate/up + down GEMM launches)",
+                     "flops_per_launch": wl.expert_flops(), "ms_per_launch": round(ffn_ms, 4)},
+        "tflops_layer": round(total_tflops, 1),
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "hbm_frac": {"permute": round(perm_bytes / (stages["permute"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "combine": round(comb_bytes / (stages["combine"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+    if args.cpu_tokens > 0:
+        out["cpu_baseline"] = cpu_baseline(torch, inp, wl, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

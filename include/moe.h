@@ -1,0 +1,155 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) routed Mixture-of-Experts layer forward.
+ *
+ * The layer (one Mixture-of-Experts block of the ~1T-parameter model in
+ * "Training a 1T-Parameter MoE on EU public infrastructure with PyTorch and
+ * TorchTitan", TL;DR, model-configuration table: hidden 6,144, 384 routed
+ * experts, top-8, expert hidden 1,792) sends every token to the k experts with
+ * the largest router logits and mixes their SwiGLU outputs:
+ *
+ *   l[t,e]  = x[t,:] . W_r[e,:] + b[e]                        (router GEMM)
+ *   S_t     = k largest l[t,:], ties to the lower expert index  (top-k)
+ *   w[t,j]  = softmax(l[t,:])[S_tj] / sum_j' softmax(l[t,:])[S_tj']
+ *   y[t]    = sum_j w[t,j] * FFN_{S_tj}(x[t])
+ *   FFN_e(v) = W_d[e] (silu(W_g[e] v) * (W_u[e] v)),  silu(z) = z/(1+exp(-z))
+ *
+ * "Domyn 团队在 Jupiter 超算完成 1 万亿参数 MoE 模型训练项目解析", section 二,
+ * states the routing idea (each token uses a few experts).  Routing is dropless
+ * (no capacity limit), as in the Pangu Ultra MoE page.  Softmax scoring, SwiGLU
+ * and the tie rule are readings the pages leave open.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  T tokens, d hidden size, E experts (on this GPU), k experts per token,
+ *  F expert hidden size.  All matrices are row-major and dense.  Weights are
+ *  stored output-major (like a linear layer): W_r [E,d], W_g and W_u [E,F,d],
+ *  W_d [E,d,F], so both operands of every GEMM are contiguous along the
+ *  contraction.
+ *  dtype (MOE_F32 or MOE_BF16) is the type of x, the expert/router weights,
+ *  x_perm, y_perm and y.  Logits, gate weights and bias are always float32;
+ *  indices are always int32.  bf16 work accumulates in float32 and rounds to
+ *  nearest-even when it stores bf16.
+ *  Every pointer is a device pointer (HBM) that the caller allocates and owns;
+ *  the library never allocates or frees device memory.  Data pointers must be
+ *  16-byte aligned; the workspace must be 256-byte aligned.
+ *  stream is a hipStream_t (NULL = the default stream).  Every call only
+ *  enqueues work on that stream and returns at once: it never synchronises and
+ *  never copies device memory to the host.  Faults inside kernels surface at
+ *  the caller's next synchronisation.
+ *  Workspace: call with ws == NULL and ws_bytes != NULL to have the required
+ *  byte count written to *ws_bytes (MOE_OK, nothing launched, no HIP call
+ *  made); call again with a buffer of at least that many bytes in ws and its
+ *  size in *ws_bytes.  ws == NULL with ws_bytes == NULL runs without a
+ *  workspace, which is allowed only when the required size is 0.
+ *  Argument checks run on the host before anything is launched.
+ *
+ * Limits: d and F multiples of 64; 1 <= k <= E <= 1024; T*k < 2^31.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null required pointer, size <= 0, k > E, misaligned pointer */
+  MOE_ERR_UNSUPPORTED = 2, /* d or F not a multiple of 64, E > 1024, T*k >= 2^31, unknown dtype */
+  MOE_ERR_WORKSPACE = 3,   /* *ws_bytes smaller than the required size, or no workspace given when one is needed */
+  MOE_ERR_HIP = 4          /* a launch or device query failed */
+} moe_status;
+
+/*
+ * moe_route: router GEMM, softmax and top-k (first two steps of the layer).
+ *   x          [T,d]  dtype      input tokens
+ *   w_router   [E,d]  dtype      router weights
+ *   bias       [E]    float32    per-expert routing bias added to the logits, or NULL
+ *   logits_out [T,E]  float32    router logits l (bias included), or NULL
+ *   topk_ids   [T,k]  int32      out: chosen experts, larger logit first, ties to the lower index
+ *   topk_w     [T,k]  float32    out: renormalised gate weights (sum 1 per token, non-increasing)
+ *   ws                           workspace: T*E*4 bytes (logits) when logits_out is NULL, else 0
+ */
+moe_status moe_route(int64_t T, int64_t d, int64_t E, int64_t k, moe_dtype dtype,
+                     const void* x, const void* w_router, const float* bias,
+                     float* logits_out, int32_t* topk_ids, float* topk_w,
+                     void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * moe_permute: group the (token, slot) pairs by expert and copy token rows.
+ *   x          [T,d]   dtype     input tokens
+ *   topk_ids   [T,k]   int32     expert of each slot; a negative id (or one >= E)
+ *                                 marks a slot whose expert is not on this GPU: it
+ *                                 is skipped.  The ids of one token must be distinct.
+ *   offsets    [E+1]   int32     out: rows offsets[e]..offsets[e+1]-1 belong to expert e;
+ *                                 offsets[E] = number of valid slots N
+ *   row_token  [T*k]   int32     out: row r copies token row_token[r]; rows of one
+ *                                 expert are in ascending token order (first N written)
+ *   slot_row   [T*k]   int32     out: row of slot (t,j), or -1 for a skipped slot
+ *   x_perm     [T*k,d] dtype     out: x_perm[r] = x[row_token[r]] (first N rows written)
+ *   ws                           workspace: ceil(T/256)*E*4 bytes
+ */
+moe_status moe_permute(int64_t T, int64_t d, int64_t E, int64_t k, moe_dtype dtype,
+                       const void* x, const int32_t* topk_ids, int32_t* offsets,
+                       int32_t* row_token, int32_t* slot_row, void* x_perm,
+                       void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * moe_grouped_ffn: the SwiGLU FFN of every expert over its own rows.
+ *   n_max              capacity (rows) of x_perm and y_perm; offsets[E] <= n_max
+ *                       is the caller's promise (the row count is read on the
+ *                       device; nothing is copied back)
+ *   x_perm   [n_max,d] dtype   rows grouped by expert
+ *   offsets  [E+1]     int32   device array as written by moe_permute; empty experts allowed
+ *   w_gate   [E,F,d]   dtype
+ *   w_up     [E,F,d]   dtype
+ *   w_down   [E,d,F]   dtype
+ *   y_perm   [n_max,d] dtype   out: y_perm[r] = W_d[e](silu(W_g[e] x_perm[r]) * (W_u[e] x_perm[r]))
+ *                               for the expert e owning row r (first offsets[E] rows)
+ *   ws                          workspace: n_max*F*sizeof(dtype) bytes (the hidden activations h)
+ */
+moe_status moe_grouped_ffn(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_dtype dtype,
+                           const void* x_perm, const int32_t* offsets,
+                           const void* w_gate, const void* w_up, const void* w_down,
+                           void* y_perm, void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * moe_combine: weighted un-permute.
+ *   y_perm    [*,d]  dtype     expert outputs by row
+ *   slot_row  [T,k]  int32     row of slot (t,j), negative = skipped
+ *   topk_w    [T,k]  float32   gate weights
+ *   y         [T,d]  dtype     out: y[t] = sum_j topk_w[t,j] * y_perm[slot_row[t,j]]
+ *                               (float32 sum); a token with no valid slot gets 0
+ */
+moe_status moe_combine(int64_t T, int64_t d, int64_t k, moe_dtype dtype,
+                       const void* y_perm, const int32_t* slot_row, const float* topk_w,
+                       void* y, void* stream);
+
+/*
+ * moe_layer_forward: the whole layer, route -> permute -> grouped FFN -> combine.
+ *   x [T,d], w_router [E,d] | NULL, bias [E] | NULL, w_gate, w_up [E,F,d], w_down [E,d,F]
+ *   y [T,d] out.
+ *   When w_router is not NULL the router runs and topk_ids / topk_w, if not
+ *   NULL, receive its choice; logits_out [T,E], if not NULL, receives the logits.
+ *   When w_router is NULL the slots are pre-routed (one expert-parallel rank's
+ *   share): topk_ids [T,k] and topk_w [T,k] are then required INPUTS, with
+ *   negative ids for slots owned elsewhere; bias and logits_out must be NULL.
+ *   offsets_out [E+1] int32, if not NULL, receives the expert row offsets.
+ *   ws: query with ws == NULL (size grows with T*k*(2d+F)).
+ */
+moe_status moe_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t F, moe_dtype dtype,
+                             const void* x, const void* w_router, const float* bias,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             void* y, float* logits_out, int32_t* topk_ids, float* topk_w,
+                             int32_t* offsets_out, void* ws, size_t* ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,194 @@
+"""Thin ctypes binding of libmoe.so.
+
+Argument marshalling only: each function takes torch device tensors, allocates
+outputs and the workspace with torch on the same device, passes raw pointers
+and the current HIP stream to the C ABI, and turns a non-zero status into an
+exception.  Every step of the layer runs in the library's HIP kernels; there is
+no fallback of any kind, and a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
+EXPORTS = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward")
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_i64, _int, _vp, _szp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
+_SIGS = {
+    "moe_route": [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp],
+    "moe_permute": [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp],
+    "moe_grouped_ffn": [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp],
+    "moe_combine": [_i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp],
+    "moe_layer_forward": [_i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                          _vp, _vp, _szp, _vp],
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return MOE_F32
+    if dt == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise MoEError(fn, st)
+
+
+def _query(fn: str, *args) -> int:
+    """Workspace size for a call (the same arguments with ws = NULL)."""
+    n = ctypes.c_size_t(0)
+    _check(fn, getattr(lib(), fn)(*args, None, ctypes.byref(n), None))
+    return n.value
+
+
+def _ws(nbytes: int, dev) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+
+def moe_route(x, w_router, k: int, bias=None, want_logits: bool = True):
+    """Router GEMM + softmax + top-k.  Returns (topk_ids, topk_w, logits|None)."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    logits = torch.empty(T, E, dtype=torch.float32, device=dev) if want_logits else None
+    head = (T, d, E, k, dtype_code(x.dtype), _p(x), _p(w_router), _p(bias), _p(logits), _p(ids), _p(w))
+    need = _query("moe_route", *head)
+    ws = _ws(need, dev)
+    n = ctypes.c_size_t(ws.numel())
+    _check("moe_route", lib().moe_route(*head, _p(ws), ctypes.byref(n), _stream(dev)))
+    return ids, w, logits
+
+
+def moe_permute(x, topk_ids, num_experts: int):
+    """Returns (offsets [E+1], row_token [T*k], slot_row [T,k], x_perm [T*k, d])."""
+    T, d = x.shape
+    k = topk_ids.shape[1]
+    dev = x.device
+    offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(T * k, dtype=torch.int32, device=dev)
+    slot_row = torch.empty(T, k, dtype=torch.int32, device=dev)
+    x_perm = torch.empty(T * k, d, dtype=x.dtype, device=dev)
+    head = (T, d, num_experts, k, dtype_code(x.dtype), _p(x), _p(topk_ids), _p(offsets), _p(row_token),
+            _p(slot_row), _p(x_perm))
+    ws = _ws(_query("moe_permute", *head), dev)
+    n = ctypes.c_size_t(ws.numel())
+    _check("moe_permute", lib().moe_permute(*head, _p(ws), ctypes.byref(n), _stream(dev)))
+    return offsets, row_token, slot_row, x_perm
+
+
+def moe_grouped_ffn(x_perm, offsets, w_gate, w_up, w_down, y_perm=None):
+    """y_perm [n_max, d]: the SwiGLU FFN of each expert over its rows."""
+    n_max, d = x_perm.shape
+    E, F, _ = w_gate.shape
+    dev = x_perm.device
+    if y_perm is None:
+        y_perm = torch.empty_like(x_perm)
+    head = (n_max, d, E, F, dtype_code(x_perm.dtype), _p(x_perm), _p(offsets), _p(w_gate), _p(w_up), _p(w_down),
+            _p(y_perm))
+    ws = _ws(_query("moe_grouped_ffn", *head), dev)
+    n = ctypes.c_size_t(ws.numel())
+    _check("moe_grouped_ffn", lib().moe_grouped_ffn(*head, _p(ws), ctypes.byref(n), _stream(dev)))
+    return y_perm
+
+
+def moe_combine(y_perm, slot_row, topk_w, out=None):
+    """y [T, d] = sum_j topk_w[t, j] * y_perm[slot_row[t, j]]."""
+    T, k = slot_row.shape
+    d = y_perm.shape[1]
+    y = torch.empty(T, d, dtype=y_perm.dtype, device=y_perm.device) if out is None else out
+    _check("moe_combine", lib().moe_combine(T, d, k, dtype_code(y_perm.dtype), _p(y_perm), _p(slot_row),
+                                            _p(topk_w), _p(y), _stream(y_perm.device)))
+    return y
+
+
+class LayerForward:
+    """moe_layer_forward with its outputs and workspace allocated once, so that
+    repeated calls (benchmarks, graph capture) allocate nothing."""
+
+    def __init__(self, x, w_router, bias, w_gate, w_up, w_down, k: int, topk_ids=None, topk_w=None,
+                 want_logits: bool = False, want_routing: bool = False, want_offsets: bool = False):
+        self.x, self.w_router, self.bias = x, w_router, bias
+        self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
+        T, d = x.shape
+        E, F, _ = w_gate.shape
+        self.T, self.d, self.E, self.k, self.F = T, d, E, k, F
+        dev = x.device
+        self.y = torch.empty(T, d, dtype=x.dtype, device=dev)
+        routed = w_router is not None
+        self.logits = torch.empty(T, E, dtype=torch.float32, device=dev) if (routed and want_logits) else None
+        if routed:
+            self.topk_ids = torch.empty(T, k, dtype=torch.int32, device=dev) if want_routing else None
+            self.topk_w = torch.empty(T, k, dtype=torch.float32, device=dev) if want_routing else None
+        else:
+            self.topk_ids, self.topk_w = topk_ids, topk_w
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if want_offsets else None
+        self._head = (T, d, E, k, F, dtype_code(x.dtype), _p(x), _p(w_router), _p(bias), _p(w_gate), _p(w_up),
+                      _p(w_down), _p(self.y), _p(self.logits), _p(self.topk_ids), _p(self.topk_w),
+                      _p(self.offsets))
+        self.ws = _ws(_query("moe_layer_forward", *self._head), dev)
+        self._n = ctypes.c_size_t(self.ws.numel())
+        self._ws_p = _p(self.ws)
+
+    def __call__(self):
+        _check("moe_layer_forward", lib().moe_layer_forward(*self._head, self._ws_p, ctypes.byref(self._n),
+                                                            _stream(self.x.device)))
+        return self.y
+
+
+def moe_layer_forward(x, w_router, bias, w_gate, w_up, w_down, k: int, topk_ids=None, topk_w=None,
+                      want_logits=False, want_routing=False, want_offsets=False):
+    """One call of the whole layer; returns the LayerForward object holding y
+    and the optional outputs."""
+    L = LayerForward(x, w_router, bias, w_gate, w_up, w_down, k, topk_ids, topk_w, want_logits, want_routing,
+                     want_offsets)
+    L()
+    return L

@@ -1,0 +1,381 @@
+// Persistent grouped "NT" GEMM for gfx950: C[r, n] = sum_k A[r, k] * B_g[n, k]
+// for every row r of group g (ragged row segments, each with its own B), with
+// an epilogue chosen at compile time.  One template serves the router GEMM
+// (one group, float32 logits plus bias), the expert gate/up GEMM (two B
+// matrices with a fused SwiGLU epilogue) and the expert down GEMM.
+//
+// Design (CDNA4):
+//  * a workgroup of WM x WN waves owns a BM x BN output tile; each wave owns a
+//    (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA blocks whose float32
+//    accumulators stay in registers for the whole K loop;
+//  * A and B k-slices travel global -> LDS with the gfx950 16-byte direct-to-LDS
+//    load (no register staging), STAGES deep; each LDS row holds BK elements
+//    (64 or 128 bytes) with its 16-byte chunks XOR-swizzled by row so that the
+//    MFMA operand reads (ds_read_b128, 32 rows at a time) hit distinct banks;
+//  * the kernel is persistent: the grid is sized to the machine and each
+//    workgroup walks tiles blockIdx.x, blockIdx.x + gridDim.x, ...  The tile
+//    list is built on the device from the group offsets (a prefix over groups
+//    of ceil(rows/BM) * column tiles), so ragged and empty groups need no host
+//    round trip; an empty group owns no tile and its weights are never read.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2 };
+
+constexpr int kMaxGroups = 1024;
+
+struct GemmArgs {
+  const void* A;          // [rows, K]; group g owns rows seg[g] .. seg[g+1]-1
+  const void* B0;         // group g: B0 + g * b_stride elements, [N, K]
+  const void* B1;         // EPI_SWIGLU: the "up" matrix, same layout as B0
+  int64_t b_stride;       // elements between two groups' B matrices
+  const int32_t* seg;     // [G+1] device row offsets; nullptr = one group, rows [0, M)
+  int32_t G;
+  int64_t M;
+  int32_t N;              // output columns
+  int32_t K;              // contraction length, a multiple of BK
+  void* C;                // [rows, N] output (row stride N)
+  const float* bias;      // EPI_F32_BIAS: [N] or nullptr
+};
+
+// Per element type: how one wave multiplies a 32x32 block over 16 k values.
+// Each lane supplies 8 consecutive (in LDS) k values of one A row and of one B
+// row; lanes 0-31 and 32-63 take the two halves of the 16.  Any assignment of
+// k values to (lane, element) is fine as long as A and B agree on it.
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16> {
+  typedef bf16x8 Frag;
+  static constexpr int kReads = 1;  // ds_read_b128 per fragment
+  __device__ __forceinline__ static void load(Frag& f, const char* p) {
+    f = *reinterpret_cast<const bf16x8*>(p);
+  }
+  __device__ __forceinline__ static void mma(const Frag& a, const Frag& b, f32x16& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float> {
+  struct Frag { f32x4 lo, hi; };
+  static constexpr int kReads = 2;
+  __device__ __forceinline__ static void load(Frag& f, const char* p0, const char* p1) {
+    f.lo = *reinterpret_cast<const f32x4*>(p0);
+    f.hi = *reinterpret_cast<const f32x4*>(p1);
+  }
+  __device__ __forceinline__ static void mma(const Frag& a, const Frag& b, f32x16& c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[i], b.lo[i], c, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[i], b.hi[i], c, 0, 0, 0);
+  }
+};
+
+// 16-byte global -> LDS copy per lane (gfx950 LDS DMA).  Lane i of the wave
+// writes LDS bytes [lds + 16 i, lds + 16 i + 16).  Issued as inline assembly so
+// the compiler neither waits on it before unrelated LDS reads nor reorders
+// memory accesses across it; completion is tracked explicitly with vmcnt.
+__device__ __forceinline__ void lds_dma16(const char* gbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(gbase), "s"(lds_addr)
+      : "memory", "m0");
+}
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// also drain every outstanding prefetch).
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const MOE_LDS char*)p);
+}
+
+// Store 4 consecutive outputs (8 bytes of bf16 or 16 bytes of float).
+__device__ __forceinline__ void store4(bf16* p, const float* v) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+  bf16x4 q;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = static_cast<bf16>(v[i]);
+  *reinterpret_cast<bf16x4*>(p) = q;
+}
+__device__ __forceinline__ void store4(float* p, const float* v) {
+  f32x4 q;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = v[i];
+  *reinterpret_cast<f32x4*>(p) = q;
+}
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI>
+struct GemmTile {
+  static constexpr int kThreads = WM * WN * 64;
+  static constexpr int RB = BK * (int)sizeof(T);      // bytes per LDS row
+  static constexpr int CPR = RB / 16;                 // 16-byte chunks per row
+  static constexpr int RP = 128 / RB;                 // rows per 128 bytes
+  static constexpr int kStageBytes = (BM + BN) * RB;
+  static constexpr int kChunks = kStageBytes / 16;
+  static constexpr int CPT = kChunks / kThreads;      // direct-to-LDS loads per thread per stage
+  static constexpr int kRowsPerStep = kThreads * 16 / RB;  // LDS rows one load step covers
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int MI = WTM / 32, NI = WTN / 32;
+  static constexpr int kSub = BK / 16;                // 16-k MFMA sub-steps per k-tile
+  static constexpr int CPL = 8 * (int)sizeof(T) / 16; // chunks per lane per fragment
+  static constexpr int NOUT = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  static constexpr int kLdsBytes = STAGES * kStageBytes;
+
+  static_assert(RB == 64 || RB == 128, "LDS row must be 64 or 128 bytes");
+  static_assert(kChunks % kThreads == 0, "stage must split evenly over threads");
+  static_assert(BM % kRowsPerStep == 0 && BN % kRowsPerStep == 0, "load steps must not straddle A and B");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be made of 32x32 blocks");
+  static_assert(EPI != EPI_SWIGLU || (NI % 2 == 0 && (BN / 2) % kRowsPerStep == 0), "SwiGLU needs paired blocks");
+  static_assert(STAGES >= 2, "need at least double buffering");
+
+  __device__ __forceinline__ static int swz(int row, int lc) { return lc ^ ((row / RP) % CPR); }
+
+  // LDS row (within the B region) that MFMA column block ni of wave column wn reads.
+  __device__ __forceinline__ static int b_row(int wn, int ni) {
+    if (EPI == EPI_SWIGLU) {
+      constexpr int H = NI / 2;
+      return ni < H ? wn * (WTN / 2) + ni * 32 : BN / 2 + wn * (WTN / 2) + (ni - H) * 32;
+    }
+    return wn * WTN + ni * 32;
+  }
+};
+
+// Exclusive prefix over groups of the number of tiles each owns, into tstart[0..G].
+template <int BM, int NTHREADS>
+__device__ void build_tile_prefix(const int32_t* seg, int G, int64_t M, int ntn, int* tstart) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int lane = tid;
+    const int per = (G + 63) / 64;
+    const int lo = min(G, lane * per), hi = min(G, lo + per);
+    int sum = 0;
+    for (int g = lo; g < hi; ++g) {
+      const int64_t rows = seg ? (int64_t)seg[g + 1] - seg[g] : M;
+      sum += (int)((rows + BM - 1) / BM) * ntn;
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    int run = incl - sum;
+    for (int g = lo; g < hi; ++g) {
+      tstart[g] = run;
+      const int64_t rows = seg ? (int64_t)seg[g + 1] - seg[g] : M;
+      run += (int)((rows + BM - 1) / BM) * ntn;
+    }
+    if (lane == 63) tstart[G] = incl;
+  }
+  __syncthreads();
+}
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI>
+__global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs p) {
+  typedef GemmTile<T, BM, BN, BK, WM, WN, STAGES, EPI> Cfg;
+  typedef Mma<T> Op;
+  constexpr int NT = Cfg::kThreads;
+  constexpr int RB = Cfg::RB;
+  constexpr int CPT = Cfg::CPT;
+  constexpr int MI = Cfg::MI, NI = Cfg::NI;
+  constexpr int NOUT = Cfg::NOUT;
+  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+
+  __shared__ __attribute__((aligned(1024))) char smem[Cfg::kLdsBytes];
+  __shared__ int tstart[kMaxGroups + 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int G = p.seg ? p.G : 1;
+  const int ntn = (p.N + NOUT - 1) / NOUT;
+  build_tile_prefix<BM, NT>(p.seg, G, p.M, ntn, tstart);
+  const int total = tstart[G];
+
+  const T* __restrict__ Abase = static_cast<const T*>(p.A);
+  const int K = p.K;
+  const int nk = K / BK;
+
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    // ---- locate the tile: group by binary search over the prefix ----------
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tstart[mid] <= tile) lo = mid; else hi = mid;
+    }
+    const int g = __builtin_amdgcn_readfirstlane(lo);
+    const int local = tile - __builtin_amdgcn_readfirstlane(tstart[g]);
+    const int mt = local / ntn, nt = local % ntn;
+    const int64_t seg_lo = p.seg ? (int64_t)p.seg[g] : 0;
+    const int64_t seg_hi = p.seg ? (int64_t)p.seg[g + 1] : p.M;
+    const int64_t m0 = seg_lo + (int64_t)mt * BM;
+    const int n0 = nt * NOUT;
+    const int rows_valid = (int)min<int64_t>(BM, seg_hi - m0);
+
+    // Uniform (SGPR) tile bases; each lane adds a fixed 32-bit byte offset, so the
+    // direct-to-LDS loads use the scalar-base + vector-offset addressing form.
+    const char* Ab = reinterpret_cast<const char*>(Abase + m0 * K);
+    const char* Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)g * p.b_stride +
+                                                    (int64_t)n0 * K);
+    const char* Bub = (EPI == EPI_SWIGLU)
+        ? reinterpret_cast<const char*>(static_cast<const T*>(p.B1) + (int64_t)g * p.b_stride + (int64_t)n0 * K)
+        : nullptr;
+
+    // ---- per-thread source offsets (bytes, relative to the tile's bases) ----
+    // Load step i covers LDS rows [i*kRowsPerStep, (i+1)*kRowsPerStep); whether it
+    // reads A, gate or up is known at compile time.
+    uint32_t soff[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int byte = (i * NT + tid) * 16;
+      const int row = byte / RB;
+      const int lc = Cfg::swz(row, (byte % RB) / 16);
+      int r;
+      if (row < BM) {
+        r = min(row, rows_valid - 1);                         // rows past the segment: any valid row
+      } else {
+        const int br = row - BM;
+        const int half = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+        const int n = (br < half) ? br : br - half;
+        r = min(n, p.N - n0 - 1);                              // columns past N: any valid column
+      }
+      soff[i] = ((uint32_t)r * (uint32_t)K + (uint32_t)(lc * EPC)) * (uint32_t)sizeof(T);
+    }
+
+    auto load_stage = [&](int stage, int k0) {
+      const uint32_t lbase = lds_addr_of(smem) + stage * Cfg::kStageBytes + wave * 64 * 16;
+      const int64_t kb = (int64_t)k0 * (int64_t)sizeof(T);
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int row0 = i * Cfg::kRowsPerStep;               // compile-time region of step i
+        const char* base;
+        if (row0 < BM) base = Ab;
+        else if (EPI == EPI_SWIGLU && row0 - BM >= BN / 2) base = Bub;
+        else base = Bgb;
+        lds_dma16(base + kb, soff[i], lbase + i * NT * 16);
+      }
+    };
+
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
+
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) load_stage(s, s * BK);
+
+    for (int kt = 0; kt < nk; ++kt) {
+      // this wave's copies for k-tile kt have landed; the barrier makes every
+      // wave's copies visible and tells all waves that stage (kt-1)%STAGES is free
+      if (kt + STAGES - 2 < nk) wait_vmcnt<(STAGES - 2) * CPT>();
+      else wait_vmcnt<0>();
+      block_barrier();
+      if (kt + STAGES - 1 < nk) load_stage((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK);
+
+      const char* sA = smem + (kt % STAGES) * Cfg::kStageBytes;
+      const char* sB = sA + BM * RB;
+#pragma unroll
+      for (int s = 0; s < Cfg::kSub; ++s) {
+        typename Op::Frag af[MI], bfr[NI];
+        const int lc0 = s * 2 * Cfg::CPL + (lane >> 5) * Cfg::CPL;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          const int r = wm * Cfg::WTM + mi * 32 + (lane & 31);
+          if constexpr (Op::kReads == 1)
+            Op::load(af[mi], sA + r * RB + Cfg::swz(r, lc0) * 16);
+          else
+            Op::load(af[mi], sA + r * RB + Cfg::swz(r, lc0) * 16, sA + r * RB + Cfg::swz(r, lc0 + 1) * 16);
+        }
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int r = Cfg::b_row(wn, ni) + (lane & 31);
+          if constexpr (Op::kReads == 1)
+            Op::load(bfr[ni], sB + r * RB + Cfg::swz(r, lc0) * 16);
+          else
+            Op::load(bfr[ni], sB + r * RB + Cfg::swz(r, lc0) * 16, sB + r * RB + Cfg::swz(r, lc0 + 1) * 16);
+        }
+        // B (weights) as the MFMA's first operand: the block comes out transposed,
+        // so each lane ends up with 4 consecutive output columns of one row.
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) Op::mma(bfr[ni], af[mi], acc[mi][ni]);
+      }
+    }
+    block_barrier();  // every wave is done with LDS before the next tile's copies
+
+    // ---- epilogue.  Block (mi, ni): lane holds output row (lane % 32) and the
+    //      columns 8*q + 4*(lane/32) + i in acc[4*q + i], q, i = 0..3 ------------
+    const int h4 = 4 * (lane >> 5);
+    if constexpr (EPI == EPI_F32_BIAS) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int r = wm * Cfg::WTM + mi * 32 + (lane & 31);
+        if (r >= rows_valid) continue;
+        float* crow = static_cast<float*>(p.C) + (m0 + r) * (int64_t)p.N;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = n0 + wn * Cfg::WTN + ni * 32 + 8 * q + h4;
+            if ((p.N & 3) == 0) {
+              if (col < p.N) {
+                f32x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = acc[mi][ni][4 * q + i] + (p.bias ? p.bias[col + i] : 0.f);
+                *reinterpret_cast<f32x4*>(crow + col) = v;
+              }
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (col + i < p.N) crow[col + i] = acc[mi][ni][4 * q + i] + (p.bias ? p.bias[col + i] : 0.f);
+            }
+          }
+      }
+    } else {
+      constexpr int NO = (EPI == EPI_SWIGLU) ? NI / 2 : NI;
+      constexpr int CW = (EPI == EPI_SWIGLU) ? Cfg::WTN / 2 : Cfg::WTN;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int r = wm * Cfg::WTM + mi * 32 + (lane & 31);
+        if (r >= rows_valid) continue;
+        T* crow = static_cast<T*>(p.C) + (m0 + r) * (int64_t)p.N;
+#pragma unroll
+        for (int ni = 0; ni < NO; ++ni)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = n0 + wn * CW + ni * 32 + 8 * q + h4;
+            if (col < p.N) {
+              float v[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                if constexpr (EPI == EPI_SWIGLU) {
+                  const float gv = acc[mi][ni][4 * q + i];
+                  const float uv = acc[mi][ni + NI / 2][4 * q + i];
+                  v[i] = gv / (1.0f + __expf(-gv)) * uv;
+                } else {
+                  v[i] = acc[mi][ni][4 * q + i];
+                }
+              }
+              store4(crow + col, v);
+            }
+          }
+      }
+    }
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,37 @@
+// Host-side launchers of the layer's kernels (one translation unit per step).
+// Every launcher only enqueues on `stream`; argument checks happen earlier,
+// in the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Router GEMM: logits[T,E] (float32) = x[T,d] . W_r[E,d]^T + bias.
+hipError_t launch_router_gemm(int dtype, int64_t T, int64_t d, int64_t E, const void* x,
+                              const void* w_router, const float* bias, float* logits,
+                              int num_cu, hipStream_t stream);
+
+// Softmax + top-k + renormalisation, one wavefront per token.
+hipError_t launch_topk(int64_t T, int64_t E, int64_t k, const float* logits, int32_t* ids,
+                       float* w, hipStream_t stream);
+
+// Permutation: counts per 256-token block, scan, stable scatter + row copy.
+hipError_t launch_permute(int dtype, int64_t T, int64_t d, int64_t E, int64_t k, const void* x,
+                          const int32_t* ids, int32_t* offsets, int32_t* row_token,
+                          int32_t* slot_row, void* x_perm, int32_t* block_counts,
+                          hipStream_t stream);
+constexpr int kPermuteBlockTokens = 256;
+
+// Grouped SwiGLU FFN: h = silu(x_perm W_g^T) * (x_perm W_u^T); y_perm = h W_d^T.
+hipError_t launch_grouped_ffn(int dtype, int64_t n_max, int64_t d, int64_t E, int64_t F,
+                              const void* x_perm, const int32_t* offsets, const void* w_gate,
+                              const void* w_up, const void* w_down, void* y_perm, void* h,
+                              int num_cu, hipStream_t stream);
+
+// Weighted un-permute: y[t] = sum_j w[t,j] * y_perm[slot_row[t,j]].
+hipError_t launch_combine(int dtype, int64_t T, int64_t d, int64_t k, const void* y_perm,
+                          const int32_t* slot_row, const float* w, void* y, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,245 @@
+// C ABI of the routed-MoE layer forward: argument checks, workspace sizing and
+// carving, launch geometry.  All checks run on the host before any HIP call, so
+// a bad call returns a status without touching the device.  Kernels are only
+// enqueued on the caller's stream; nothing here synchronises or allocates.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "kernels.h"
+#include "moe.h"
+
+namespace {
+
+constexpr int64_t kMaxE = 1024;
+constexpr int64_t kMaxDim = int64_t(1) << 20;
+constexpr int64_t kIdxLimit = int64_t(1) << 31;
+constexpr size_t kWsAlign = 256;
+
+size_t round_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool ok16(const void* p) { return p != nullptr && aligned(p, 16); }
+bool ok4(const void* p) { return p != nullptr && aligned(p, 4); }
+bool opt16(const void* p) { return p == nullptr || aligned(p, 16); }
+bool opt4(const void* p) { return p == nullptr || aligned(p, 4); }
+size_t elem_size(moe_dtype t) { return t == MOE_BF16 ? 2 : 4; }
+
+// Compute units of the current device, cached per device.
+std::atomic<int> g_cu_cache[64];
+
+moe_status num_cu(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev >= 0 && dev < 64) {
+    const int c = g_cu_cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return MOE_OK;
+    }
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return MOE_ERR_HIP;
+  if (dev >= 0 && dev < 64) g_cu_cache[dev].store(n, std::memory_order_relaxed);
+  *out = n;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status check_dtype(moe_dtype t) { return (t == MOE_F32 || t == MOE_BF16) ? MOE_OK : MOE_ERR_UNSUPPORTED; }
+
+// Shared size checks for T, d, E, k.
+moe_status check_tdek(int64_t T, int64_t d, int64_t E, int64_t k) {
+  if (T <= 0 || d <= 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_INVALID_ARG;
+  if (d % 64 != 0 || d > kMaxDim || E > kMaxE || T * k >= kIdxLimit) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_ffn_dims(int64_t n_max, int64_t d, int64_t E, int64_t F) {
+  if (n_max <= 0 || d <= 0 || E <= 0 || F <= 0) return MOE_ERR_INVALID_ARG;
+  if (d % 64 != 0 || F % 64 != 0 || d > kMaxDim || F > kMaxDim || E > kMaxE || n_max >= kIdxLimit)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t permute_ws(int64_t T, int64_t E) {
+  const int64_t nblk = (T + moe::kPermuteBlockTokens - 1) / moe::kPermuteBlockTokens;
+  return round_up((size_t)nblk * (size_t)E * 4);
+}
+
+// Resolve the workspace protocol: query (ws == NULL) or size check.
+// Returns true when the caller should return `st` right away.
+// ws == NULL with ws_bytes == NULL means "no workspace provided": fine only
+// when none is needed.
+bool workspace_step(void* ws, size_t* ws_bytes, size_t need, moe_status* st) {
+  if (ws_bytes == nullptr) {
+    if (ws == nullptr && need == 0) return false;
+    *st = MOE_ERR_WORKSPACE;
+    return true;
+  }
+  if (ws == nullptr) {
+    *ws_bytes = need;
+    *st = MOE_OK;
+    return true;
+  }
+  if (*ws_bytes < need) {
+    *st = MOE_ERR_WORKSPACE;
+    return true;
+  }
+  if (!aligned(ws, kWsAlign)) {
+    *st = MOE_ERR_INVALID_ARG;
+    return true;
+  }
+  return false;
+}
+
+// Carves consecutive 256-byte aligned pieces out of the workspace.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* ws) : base(static_cast<char*>(ws)) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + used : nullptr;
+    used += round_up(bytes);
+    return p;
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_route(int64_t T, int64_t d, int64_t E, int64_t k, moe_dtype dtype, const void* x,
+                     const void* w_router, const float* bias, float* logits_out, int32_t* topk_ids, float* topk_w,
+                     void* ws, size_t* ws_bytes, void* stream) {
+  moe_status st = check_tdek(T, d, E, k);
+  if (st != MOE_OK) return st;
+  if ((st = check_dtype(dtype)) != MOE_OK) return st;
+  const size_t need = logits_out ? 0 : round_up((size_t)T * (size_t)E * 4);
+  if (ws == nullptr && ws_bytes != nullptr) {
+    *ws_bytes = need;
+    return MOE_OK;
+  }
+  if (!ok16(x) || !ok16(w_router) || !opt4(bias) || !opt16(logits_out) || !ok4(topk_ids) || !ok4(topk_w))
+    return MOE_ERR_INVALID_ARG;
+  if (workspace_step(ws, ws_bytes, need, &st)) return st;
+  int ncu = 0;
+  if ((st = num_cu(&ncu)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* logits = logits_out ? logits_out : static_cast<float*>(ws);
+  if ((st = hip_status(moe::launch_router_gemm(dtype, T, d, E, x, w_router, bias, logits, ncu, s))) != MOE_OK)
+    return st;
+  return hip_status(moe::launch_topk(T, E, k, logits, topk_ids, topk_w, s));
+}
+
+moe_status moe_permute(int64_t T, int64_t d, int64_t E, int64_t k, moe_dtype dtype, const void* x,
+                       const int32_t* topk_ids, int32_t* offsets, int32_t* row_token, int32_t* slot_row,
+                       void* x_perm, void* ws, size_t* ws_bytes, void* stream) {
+  moe_status st = check_tdek(T, d, E, k);
+  if (st != MOE_OK) return st;
+  if ((st = check_dtype(dtype)) != MOE_OK) return st;
+  const size_t need = permute_ws(T, E);
+  if (ws == nullptr && ws_bytes != nullptr) {
+    *ws_bytes = need;
+    return MOE_OK;
+  }
+  if (!ok16(x) || !ok4(topk_ids) || !ok4(offsets) || !ok4(row_token) || !ok4(slot_row) || !ok16(x_perm))
+    return MOE_ERR_INVALID_ARG;
+  if (workspace_step(ws, ws_bytes, need, &st)) return st;
+  return hip_status(moe::launch_permute(dtype, T, d, E, k, x, topk_ids, offsets, row_token, slot_row, x_perm,
+                                        static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_grouped_ffn(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_dtype dtype, const void* x_perm,
+                           const int32_t* offsets, const void* w_gate, const void* w_up, const void* w_down,
+                           void* y_perm, void* ws, size_t* ws_bytes, void* stream) {
+  moe_status st = check_ffn_dims(n_max, d, E, F);
+  if (st != MOE_OK) return st;
+  if ((st = check_dtype(dtype)) != MOE_OK) return st;
+  const size_t need = round_up((size_t)n_max * (size_t)F * elem_size(dtype));
+  if (ws == nullptr && ws_bytes != nullptr) {
+    *ws_bytes = need;
+    return MOE_OK;
+  }
+  if (!ok16(x_perm) || !ok4(offsets) || !ok16(w_gate) || !ok16(w_up) || !ok16(w_down) || !ok16(y_perm))
+    return MOE_ERR_INVALID_ARG;
+  if (workspace_step(ws, ws_bytes, need, &st)) return st;
+  int ncu = 0;
+  if ((st = num_cu(&ncu)) != MOE_OK) return st;
+  return hip_status(moe::launch_grouped_ffn(dtype, n_max, d, E, F, x_perm, offsets, w_gate, w_up, w_down, y_perm,
+                                            ws, ncu, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_combine(int64_t T, int64_t d, int64_t k, moe_dtype dtype, const void* y_perm,
+                       const int32_t* slot_row, const float* topk_w, void* y, void* stream) {
+  if (T <= 0 || d <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
+  if (d % 64 != 0 || d > kMaxDim || T * k >= kIdxLimit) return MOE_ERR_UNSUPPORTED;
+  moe_status st = check_dtype(dtype);
+  if (st != MOE_OK) return st;
+  if (!ok16(y_perm) || !ok4(slot_row) || !ok4(topk_w) || !ok16(y)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine(dtype, T, d, k, y_perm, slot_row, topk_w, y,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t F, moe_dtype dtype, const void* x,
+                             const void* w_router, const float* bias, const void* w_gate, const void* w_up,
+                             const void* w_down, void* y, float* logits_out, int32_t* topk_ids, float* topk_w,
+                             int32_t* offsets_out, void* ws, size_t* ws_bytes, void* stream) {
+  moe_status st = check_tdek(T, d, E, k);
+  if (st != MOE_OK) return st;
+  if (F <= 0) return MOE_ERR_INVALID_ARG;
+  if (F % 64 != 0 || F > kMaxDim) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_dtype(dtype)) != MOE_OK) return st;
+  const bool routed = w_router != nullptr;
+  const size_t es = elem_size(dtype);
+  const size_t slots = (size_t)T * (size_t)k;
+
+  // workspace layout (each piece 256-byte aligned)
+  Carver c(ws);
+  float* logits = routed ? (logits_out ? logits_out : static_cast<float*>(c.take((size_t)T * E * 4))) : nullptr;
+  int32_t* ids = (routed && !topk_ids) ? static_cast<int32_t*>(c.take(slots * 4)) : topk_ids;
+  float* w = (routed && !topk_w) ? static_cast<float*>(c.take(slots * 4)) : topk_w;
+  int32_t* offsets = offsets_out ? offsets_out : static_cast<int32_t*>(c.take((size_t)(E + 1) * 4));
+  int32_t* row_token = static_cast<int32_t*>(c.take(slots * 4));
+  int32_t* slot_row = static_cast<int32_t*>(c.take(slots * 4));
+  int32_t* counts = static_cast<int32_t*>(c.take(permute_ws(T, E)));
+  void* x_perm = c.take(slots * (size_t)d * es);   // later reused for y_perm
+  void* h = c.take(slots * (size_t)F * es);
+  const size_t need = c.used;
+
+  if (ws == nullptr && ws_bytes != nullptr) {
+    *ws_bytes = need;
+    return MOE_OK;
+  }
+  if (!ok16(x) || !ok16(w_gate) || !ok16(w_up) || !ok16(w_down) || !ok16(y) || !opt16(logits_out) ||
+      !opt4(offsets_out))
+    return MOE_ERR_INVALID_ARG;
+  if (routed) {
+    if (!ok16(w_router) || !opt4(bias) || !opt4(topk_ids) || !opt4(topk_w)) return MOE_ERR_INVALID_ARG;
+  } else {
+    if (bias || logits_out || !ok4(topk_ids) || !ok4(topk_w)) return MOE_ERR_INVALID_ARG;
+  }
+  if (workspace_step(ws, ws_bytes, need, &st)) return st;
+  int ncu = 0;
+  if ((st = num_cu(&ncu)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (routed) {
+    if ((st = hip_status(moe::launch_router_gemm(dtype, T, d, E, x, w_router, bias, logits, ncu, s))) != MOE_OK)
+      return st;
+    if ((st = hip_status(moe::launch_topk(T, E, k, logits, ids, w, s))) != MOE_OK) return st;
+  }
+  if ((st = hip_status(moe::launch_permute(dtype, T, d, E, k, x, ids, offsets, row_token, slot_row, x_perm, counts,
+                                           s))) != MOE_OK)
+    return st;
+  // y_perm overwrites x_perm: the down GEMM runs after the gate/up GEMM has
+  // finished reading x_perm (same stream).
+  if ((st = hip_status(moe::launch_grouped_ffn(dtype, (int64_t)slots, d, E, F, x_perm, offsets, w_gate, w_up, w_down,
+                                               x_perm, h, ncu, s))) != MOE_OK)
+    return st;
+  return hip_status(moe::launch_combine(dtype, T, d, k, x_perm, slot_row, w, y, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+"""The three full-size workloads, through the same entry point and launch
+configuration that bench.py times (moe_layer_forward).  The oracle checks:
+  * routing of EVERY token: ids bit-exact and gate weights within 1e-6 when the
+    oracle selects on the GPU's logits; the logits themselves on a token sample;
+  * the expert offsets, bit-exact;
+  * the grouped FFN on sampled rows of sampled experts (stage entry points);
+  * the layer output on sampled tokens;
+  * the layer entry point equals the stage-by-stage path bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_16_amd import binding as B
+from mixture_experts_layer_16_amd import workloads as W
+from oracle import moe_oracle as orc
+from parity_util import assert_close, assert_logits_close, bits_equal, f64, i64, routing_disagreement
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+FULL = ["page_balanced", "page_seq64k_skewed", "ep_rank_share"]
+
+
+class ExpertCache:
+    """float64 host copies of whole experts, fetched once each."""
+
+    def __init__(self, inp):
+        self.inp, self.c = inp, {}
+
+    def __call__(self, e):
+        if e not in self.c:
+            self.c[e] = tuple(f64(self.inp[n][e]) for n in ("w_gate", "w_up", "w_down"))
+        return self.c[e]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_parity(name):
+    wl = W.WORKLOADS[name]
+    print(f"[full-size] {name}: T={wl.T} d={wl.d} E={wl.E} k={wl.k} F={wl.F}", flush=True)
+    inp = W.make_inputs(wl, device=DEV)
+    routed = inp["w_router"] is not None
+    L = B.LayerForward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"], inp["w_down"], wl.k,
+                       topk_ids=inp.get("topk_ids"), topk_w=inp.get("topk_w"), want_logits=routed,
+                       want_routing=routed, want_offsets=True)
+    L()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    T = wl.T
+
+    if routed:
+        gl = L.logits.cpu().numpy().astype(np.float64)
+        ref_ids, ref_w = orc.select_topk(gl, wl.k)
+        assert np.array_equal(i64(L.topk_ids), ref_ids)
+        assert np.abs(f64(L.topk_w) - ref_w).max() <= 1e-6
+        S = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 62, replace=False)]))
+        own = orc.router_logits(f64(inp["x"][S]), f64(inp["w_router"]), f64(inp["bias"]))
+        assert_logits_close(gl[S], own, wl.dtype)
+        routing_disagreement(own, gl[S], wl.k)
+    else:
+        ref_ids, ref_w = i64(inp["topk_ids"]), f64(inp["topk_w"])
+    r_off, r_rt, r_sr = orc.permute(ref_ids, wl.E)
+    assert np.array_equal(i64(L.offsets), r_off)
+    counts = np.diff(r_off)
+    print(f"[full-size] {name}: expert rows min {counts.min()} max {counts.max()} empty {(counts == 0).sum()}",
+          flush=True)
+
+    experts = ExpertCache(inp)
+
+    # layer output on sampled tokens (tokens with no local slot included when present)
+    has = (ref_ids >= 0).any(1)
+    St = list(rng.choice(np.nonzero(has)[0], 6, replace=False))
+    if (~has).any():
+        St.append(int(np.nonzero(~has)[0][0]))
+    xs = f64(inp["x"][St])
+    y_ref = np.zeros((len(St), wl.d))
+    for i, t in enumerate(St):
+        for j in range(wl.k):
+            e = int(ref_ids[t, j])
+            if e >= 0:
+                y_ref[i] += ref_w[t, j] * orc.expert_ffn(xs[i:i + 1], *experts(e))[0]
+    assert_close(f64(L.y[St]), y_ref, wl.dtype, "y (sampled tokens)")
+
+    # the stage entry points: bit-equal to the layer entry point, and the grouped
+    # FFN on sampled rows of the largest, the smallest non-empty and two random experts
+    if routed:
+        ids, w, _ = B.moe_route(inp["x"], inp["w_router"], wl.k, bias=inp["bias"], want_logits=False)
+    else:
+        ids, w = inp["topk_ids"], inp["topk_w"]
+    off, rt, sr, xp = B.moe_permute(inp["x"], ids, wl.E)
+    yp = B.moe_grouped_ffn(xp, off, inp["w_gate"], inp["w_up"], inp["w_down"])
+    del xp
+    y = B.moe_combine(yp, sr, w)
+    torch.cuda.synchronize()
+    assert bits_equal(y, L.y)
+    nz = np.nonzero(counts)[0]
+    pick = {int(np.argmax(counts)), int(nz[np.argmin(counts[nz])])} | set(rng.choice(nz, 2, replace=False).tolist())
+    for e in sorted(pick):
+        lo, hi = int(r_off[e]), int(r_off[e + 1])
+        rows = np.unique(np.concatenate([[lo, hi - 1], rng.integers(lo, hi, 14)]))
+        ref = orc.expert_ffn(f64(inp["x"][torch.from_numpy(r_rt[rows].astype(np.int64)).to(DEV)]), *experts(e))
+        assert_close(f64(yp[torch.from_numpy(rows).to(DEV)]), ref, wl.dtype, f"y_perm rows of expert {e}")

@@ -1,0 +1,265 @@
+"""HIP path against the float64 CPU oracle, stage by stage and for the whole
+layer, at sizes the oracle finishes in seconds (several tiles, ragged tails,
+empty experts), plus the method's degenerate cases.  All calls go through the
+C ABI (libmoe.so)."""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_16_amd import binding as B
+from mixture_experts_layer_16_amd import workloads as W
+from oracle import moe_oracle as orc
+from parity_util import (LazyExperts, assert_close, assert_logits_close, bits_equal, f64, i64,
+                         routing_disagreement)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+# shapes that cross tile edges: 256-row M tiles, 128-column gate/up tiles,
+# 256-column down tiles, and tails in each
+RAGGED = [
+    W.Workload("ragged_a", T=777, d=192, E=11, k=3, F=192, dtype=torch.bfloat16),
+    W.Workload("ragged_b", T=1000, d=320, E=6, k=2, F=320, dtype=torch.bfloat16),
+    W.Workload("ragged_fp32", T=513, d=128, E=5, k=2, F=64, dtype=torch.float32),
+    W.Workload("wide_E", T=600, d=256, E=384, k=8, F=128, dtype=torch.bfloat16, router_std=0.02,
+               routing="router_bias"),
+]
+SMALL = [W.WORKLOADS["tiny_fp32"], W.WORKLOADS["small_bf16"]] + RAGGED
+
+
+def _inputs(wl, seed=0):
+    return W.make_inputs(wl, device=DEV, seed=seed)
+
+
+def _run_layer(inp, wl):
+    L = B.moe_layer_forward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"], inp["w_down"],
+                            wl.k, topk_ids=inp.get("topk_ids"), topk_w=inp.get("topk_w"),
+                            want_logits=inp["w_router"] is not None, want_routing=inp["w_router"] is not None,
+                            want_offsets=True)
+    torch.cuda.synchronize()
+    return L
+
+
+# ---------------------------------------------------------------------------
+# route
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_route_matches_oracle(wl):
+    inp = _inputs(wl)
+    ids, w, logits = B.moe_route(inp["x"], inp["w_router"], wl.k, bias=inp["bias"])
+    torch.cuda.synchronize()
+    gl = logits.cpu().numpy().astype(np.float64)
+    own = orc.router_logits(f64(inp["x"]), f64(inp["w_router"]), f64(inp["bias"]))
+    assert_logits_close(gl, own, wl.dtype)
+    ref_ids, ref_w = orc.select_topk(gl, wl.k)
+    assert np.array_equal(i64(ids), ref_ids)
+    assert np.abs(f64(w) - ref_w).max() <= 1e-6
+    assert np.abs(f64(w).sum(1) - 1.0).max() <= 1e-6
+    routing_disagreement(own, gl, wl.k)
+
+
+def test_route_without_logits_output_matches():
+    wl = RAGGED[0]
+    inp = _inputs(wl)
+    ids1, w1, _ = B.moe_route(inp["x"], inp["w_router"], wl.k, want_logits=False)
+    ids2, w2, _ = B.moe_route(inp["x"], inp["w_router"], wl.k, want_logits=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ids1, ids2) and bits_equal(w1, w2)
+
+
+# ---------------------------------------------------------------------------
+# permute
+# ---------------------------------------------------------------------------
+
+def _random_ids(T, E, k, drop, seed):
+    r = np.random.default_rng(seed)
+    ids = np.stack([r.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ids[r.random((T, k)) < drop] = -1
+    return ids
+
+
+@pytest.mark.parametrize("T,E,k,drop,dtype", [
+    (1000, 37, 5, 0.0, torch.bfloat16), (1000, 37, 5, 0.3, torch.bfloat16), (513, 1, 1, 0.0, torch.float32),
+    (300, 1024, 16, 0.1, torch.bfloat16), (4096, 64, 8, 0.0, torch.bfloat16), (1, 8, 8, 0.0, torch.float32),
+    (257, 16, 16, 0.5, torch.bfloat16), (100, 50, 3, 1.0, torch.bfloat16),
+])
+def test_permute_bit_exact(T, E, k, drop, dtype):
+    ids = _random_ids(T, E, k, drop, seed=T + E)
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    x = torch.randn(T, 128, generator=gen, device=DEV).to(dtype)
+    off, rt, sr, xp = B.moe_permute(x, torch.from_numpy(ids).to(DEV), E)
+    torch.cuda.synchronize()
+    r_off, r_rt, r_sr = orc.permute(ids, E)
+    N = int(r_off[-1])
+    assert np.array_equal(i64(off), r_off)
+    assert np.array_equal(i64(rt)[:N], r_rt)
+    assert np.array_equal(i64(sr), r_sr)
+    idx = torch.from_numpy(r_rt.astype(np.int64)).to(DEV)
+    assert bits_equal(xp[:N], x[idx])
+
+
+# ---------------------------------------------------------------------------
+# grouped FFN
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("counts,d,F,dtype", [
+    ([0, 1, 255, 256, 257, 0, 600, 3], 256, 192, torch.bfloat16),
+    ([513, 0, 0, 40], 320, 320, torch.bfloat16),
+    ([1, 2, 300, 0, 64], 128, 64, torch.float32),
+    ([1000], 512, 256, torch.bfloat16),
+    ([0, 0, 7], 64, 64, torch.bfloat16),
+])
+def test_grouped_ffn_matches_oracle(counts, d, F, dtype):
+    E = len(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(off[-1])
+    n_max = N + 37                                   # spare rows beyond the last expert
+    gen = torch.Generator(device=DEV).manual_seed(11)
+    xp = torch.randn(n_max, d, generator=gen, device=DEV).to(dtype)
+    wg = (torch.randn(E, F, d, generator=gen, device=DEV) / d ** 0.5).to(dtype)
+    wu = (torch.randn(E, F, d, generator=gen, device=DEV) / d ** 0.5).to(dtype)
+    wd = (torch.randn(E, d, F, generator=gen, device=DEV) / F ** 0.5).to(dtype)
+    yp = B.moe_grouped_ffn(xp, torch.from_numpy(off).to(DEV), wg, wu, wd)
+    torch.cuda.synchronize()
+    ref = orc.grouped_ffn(f64(xp[:N]), off, LazyExperts(wg), LazyExperts(wu), LazyExperts(wd))
+    assert_close(f64(yp[:N]), ref, dtype, "y_perm")
+
+
+def test_grouped_ffn_in_place_over_x_perm():
+    counts, d, F = [300, 0, 5], 128, 128
+    off = torch.tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), device=DEV)
+    gen = torch.Generator(device=DEV).manual_seed(12)
+    xp = torch.randn(305, d, generator=gen, device=DEV).to(torch.bfloat16)
+    w = [(torch.randn(3, F, d, generator=gen, device=DEV) / d ** 0.5).to(torch.bfloat16) for _ in range(2)]
+    wd = (torch.randn(3, d, F, generator=gen, device=DEV) / F ** 0.5).to(torch.bfloat16)
+    ref = B.moe_grouped_ffn(xp, off, w[0], w[1], wd)
+    xp2 = xp.clone()
+    B.moe_grouped_ffn(xp2, off, w[0], w[1], wd, y_perm=xp2)
+    torch.cuda.synchronize()
+    assert bits_equal(ref, xp2)
+
+
+# ---------------------------------------------------------------------------
+# combine
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,k,d,drop,dtype", [(1000, 37, 5, 256, 0.2, torch.bfloat16),
+                                                (300, 8, 2, 64, 0.0, torch.float32),
+                                                (50, 10, 10, 128, 0.9, torch.bfloat16)])
+def test_combine_matches_oracle(T, E, k, d, drop, dtype):
+    ids = _random_ids(T, E, k, drop, seed=3)
+    _, _, sr = orc.permute(ids, E)
+    N = int((ids >= 0).sum())
+    gen = torch.Generator(device=DEV).manual_seed(13)
+    yp = torch.randn(max(N, 1), d, generator=gen, device=DEV).to(dtype)
+    w = torch.rand(T, k, generator=gen, device=DEV)
+    y = B.moe_combine(yp, torch.from_numpy(sr).to(DEV), w)
+    torch.cuda.synchronize()
+    ref = orc.combine(f64(yp), sr, f64(w))
+    assert_close(f64(y), ref, dtype, "y")
+    assert np.all(f64(y)[(ids < 0).all(1)] == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# whole layer
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_layer_forward_matches_oracle(wl):
+    inp = _inputs(wl)
+    L = _run_layer(inp, wl)
+    gl = L.logits.cpu().numpy().astype(np.float64)
+    ref = orc.layer_forward(f64(inp["x"]), f64(inp["w_router"]), f64(inp["bias"]), LazyExperts(inp["w_gate"]),
+                            LazyExperts(inp["w_up"]), LazyExperts(inp["w_down"]), wl.k, selection_logits=gl)
+    assert np.array_equal(i64(L.topk_ids), ref["ids"])
+    assert np.array_equal(i64(L.offsets), ref["offsets"])
+    assert np.abs(f64(L.topk_w) - ref["w"]).max() <= 1e-6
+    assert_close(f64(L.y), ref["y"], wl.dtype, "y")
+    assert_logits_close(gl, ref["logits"], wl.dtype)
+    routing_disagreement(ref["logits"], gl, wl.k)
+
+
+def test_layer_forward_equals_stage_by_stage():
+    wl = RAGGED[0]
+    inp = _inputs(wl)
+    L = _run_layer(inp, wl)
+    ids, w, _ = B.moe_route(inp["x"], inp["w_router"], wl.k)
+    off, rt, sr, xp = B.moe_permute(inp["x"], ids, wl.E)
+    yp = B.moe_grouped_ffn(xp, off, inp["w_gate"], inp["w_up"], inp["w_down"])
+    y = B.moe_combine(yp, sr, w)
+    torch.cuda.synchronize()
+    assert bits_equal(L.y, y)
+
+
+PRE_ROUTED = [W.Workload("pre_small", T=2000, d=256, E=24, k=8, F=192, dtype=torch.bfloat16, routing="pre_routed",
+                         n_slots=3000, n_empty=3, hot_frac=0.2),
+              W.Workload("pre_fp32", T=300, d=128, E=6, k=4, F=64, dtype=torch.float32, routing="pre_routed",
+                         n_slots=500, n_empty=1, hot_frac=0.4)]
+
+
+@pytest.mark.parametrize("wl", PRE_ROUTED, ids=[w.name for w in PRE_ROUTED])
+def test_pre_routed_layer_matches_oracle(wl):
+    inp = _inputs(wl)
+    L = _run_layer(inp, wl)
+    ids = i64(inp["topk_ids"])
+    ref = orc.layer_forward(f64(inp["x"]), None, None, LazyExperts(inp["w_gate"]), LazyExperts(inp["w_up"]),
+                            LazyExperts(inp["w_down"]), wl.k, ids=ids, weights=f64(inp["topk_w"]))
+    assert np.array_equal(i64(L.offsets), ref["offsets"])
+    assert_close(f64(L.y), ref["y"], wl.dtype, "y")
+    assert np.all(f64(L.y)[(ids < 0).all(1)] == 0.0)
+
+
+def test_two_runs_are_bitwise_identical():
+    wl = W.WORKLOADS["small_bf16"]
+    inp = _inputs(wl)
+    a = _run_layer(inp, wl)
+    ya, ida = a.y.clone(), a.topk_ids.clone()
+    a()
+    torch.cuda.synchronize()
+    assert bits_equal(ya, a.y) and torch.equal(ida, a.topk_ids)
+
+
+# ---------------------------------------------------------------------------
+# degenerate cases of the method
+# ---------------------------------------------------------------------------
+
+def _layer_vs_oracle(inp, wl):
+    L = _run_layer(inp, wl)
+    gl = L.logits.cpu().numpy().astype(np.float64)
+    ref = orc.layer_forward(f64(inp["x"]), f64(inp["w_router"]), f64(inp["bias"]), LazyExperts(inp["w_gate"]),
+                            LazyExperts(inp["w_up"]), LazyExperts(inp["w_down"]), wl.k, selection_logits=gl)
+    assert np.array_equal(i64(L.topk_ids), ref["ids"])
+    assert_close(f64(L.y), ref["y"], wl.dtype, "y")
+    return L, ref
+
+
+@pytest.mark.parametrize("T,E,k", [(300, 16, 1), (300, 8, 8), (300, 1, 1), (1, 4, 2), (16, 64, 2)])
+def test_k_and_E_extremes(T, E, k):
+    wl = W.Workload("edge", T=T, d=128, E=E, k=k, F=128, dtype=torch.bfloat16)
+    L, ref = _layer_vs_oracle(_inputs(wl, seed=T + E + k), wl)
+    if k == 1:
+        assert np.all(f64(L.topk_w) == 1.0)
+
+
+def test_equal_logits_pick_lowest_indices():
+    wl = W.Workload("ties", T=200, d=128, E=12, k=3, F=64, dtype=torch.bfloat16)
+    inp = _inputs(wl)
+    inp["w_router"].zero_()
+    L, _ = _layer_vs_oracle(inp, wl)
+    assert np.array_equal(i64(L.topk_ids), np.broadcast_to(np.arange(3), (200, 3)))
+    assert np.abs(f64(L.topk_w) - 1.0 / 3.0).max() <= 1e-6
+
+
+def test_identity_router_crafts_exact_ties():
+    # d == E and W_r = I: the logits are x itself (one exact product per dot
+    # product), so crafted equal values (and -0.0 vs +0.0) are exact ties.
+    E = 64
+    wl = W.Workload("eye", T=256, d=E, E=E, k=5, F=64, dtype=torch.bfloat16)
+    inp = _inputs(wl)
+    r = np.random.default_rng(21)
+    vals = r.choice(np.array([-1.0, -0.0, 0.0, 0.5, 0.5, 1.0, 2.0], dtype=np.float32), size=(256, E))
+    inp["x"] = torch.from_numpy(vals).to(DEV).to(torch.bfloat16)
+    inp["w_router"] = torch.eye(E, device=DEV, dtype=torch.bfloat16)
+    L, _ = _layer_vs_oracle(inp, wl)
+    assert np.array_equal(L.logits.cpu().numpy() + 0.0, vals + 0.0)
