@@ -11,7 +11,7 @@
 //  * A and B k-slices travel global -> LDS with the gfx950 16-byte direct-to-LDS
 //    load (no register staging), STAGES deep; each LDS row holds BK elements
 //    (64 or 128 bytes) with its 16-byte chunks XOR-swizzled by row so that the
-//    MFMA operand reads (ds_read_b128, 32 rows at a time) hit distinct banks;
+//    MFMA operand reads (ds_read_b128, 16 rows per LDS cycle) hit distinct banks;
 //  * the kernel is persistent: the grid is sized to the machine and each
 //    workgroup walks tiles blockIdx.x, blockIdx.x + gridDim.x, ...  The tile
 //    list is built on the device from the group offsets (a prefix over groups
@@ -26,6 +26,7 @@ namespace moe {
 enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2 };
 
 constexpr int kMaxGroups = 1024;
+constexpr int kXcds = 8;   // accelerator complex dies of an MI355X, one L2 each
 
 struct GemmArgs {
   const void* A;          // [rows, K]; group g owns rows seg[g] .. seg[g+1]-1
@@ -39,6 +40,7 @@ struct GemmArgs {
   int32_t K;              // contraction length, a multiple of BK
   void* C;                // [rows, N] output (row stride N)
   const float* bias;      // EPI_F32_BIAS: [N] or nullptr
+  int32_t n_group;        // tile order: column tiles per group (<= 0: all columns of a row tile)
 };
 
 // Per element type: how one wave multiplies a 32x32 block over 16 k values.
@@ -77,17 +79,23 @@ template <> struct Mma<float> {
 // writes LDS bytes [lds + 16 i, lds + 16 i + 16).  Issued as inline assembly so
 // the compiler neither waits on it before unrelated LDS reads nor reorders
 // memory accesses across it; completion is tracked explicitly with vmcnt.
+// M0 (which holds the LDS destination) is saved and restored around the copy, so
+// the compiler's own view of M0 stays valid.
 __device__ __forceinline__ void lds_dma16(const char* gbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
   asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
       : "v"(voff), "s"(gbase), "s"(lds_addr)
-      : "memory", "m0");
+      : "memory");
 }
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 // Workgroup barrier without the memory fence of __syncthreads (which would
 // also drain every outstanding prefetch).
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -116,7 +124,7 @@ struct GemmTile {
   static constexpr int kThreads = WM * WN * 64;
   static constexpr int RB = BK * (int)sizeof(T);      // bytes per LDS row
   static constexpr int CPR = RB / 16;                 // 16-byte chunks per row
-  static constexpr int RP = 128 / RB;                 // rows per 128 bytes
+  static constexpr int RP = 256 / RB;                 // rows per 256-byte LDS bank window
   static constexpr int kStageBytes = (BM + BN) * RB;
   static constexpr int kChunks = kStageBytes / 16;
   static constexpr int CPT = kChunks / kThreads;      // direct-to-LDS loads per thread per stage
@@ -135,6 +143,10 @@ struct GemmTile {
   static_assert(EPI != EPI_SWIGLU || (NI % 2 == 0 && (BN / 2) % kRowsPerStep == 0), "SwiGLU needs paired blocks");
   static_assert(STAGES >= 2, "need at least double buffering");
 
+  // gfx950 serves a ds_read_b128 16 lanes at a time across 64 four-byte banks (a
+  // 256-byte window).  The 16 lanes of a group read 16 consecutive rows at the
+  // same logical chunk; XOR-ing the chunk with (row / RP) % CPR puts them in 16
+  // distinct 16-byte slots of the window.
   __device__ __forceinline__ static int swz(int row, int lc) { return lc ^ ((row / RP) % CPR); }
 
   // LDS row (within the B region) that MFMA column block ni of wave column wn reads.
@@ -177,7 +189,8 @@ __device__ void build_tile_prefix(const int32_t* seg, int G, int64_t M, int ntn,
   __syncthreads();
 }
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI>
+// PD: how many 16-k sub-steps ahead the MFMA operand fragments are read from LDS.
+template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, int PD = 1>
 __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs p) {
   typedef GemmTile<T, BM, BN, BK, WM, WN, STAGES, EPI> Cfg;
   typedef Mma<T> Op;
@@ -186,7 +199,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   constexpr int CPT = Cfg::CPT;
   constexpr int MI = Cfg::MI, NI = Cfg::NI;
   constexpr int NOUT = Cfg::NOUT;
-  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
+  constexpr int KSUB = Cfg::kSub;
+  static_assert(PD >= 1 && PD < KSUB, "prefetch distance must be 1 .. sub-steps - 1");
 
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::kLdsBytes];
   __shared__ int tstart[kMaxGroups + 1];
@@ -199,43 +214,53 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   const int G = p.seg ? p.G : 1;
   const int ntn = (p.N + NOUT - 1) / NOUT;
   build_tile_prefix<BM, NT>(p.seg, G, p.M, ntn, tstart);
-  const int total = tstart[G];
-
-  const T* __restrict__ Abase = static_cast<const T*>(p.A);
+  const int total = __builtin_amdgcn_readfirstlane(tstart[G]);
   const int K = p.K;
   const int nk = K / BK;
+  const T* __restrict__ Abase = static_cast<const T*>(p.A);
 
-  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-    // ---- locate the tile: group by binary search over the prefix ----------
-    int lo = 0, hi = G;
+  // ---- tile bookkeeping (all wave-uniform) ------------------------------------
+  int g = 0, n0 = 0, rows_valid = 0;
+  int64_t m0 = 0;
+  auto locate = [&](int tile) {
+    int lo = 0, hi = G;                      // largest g with tstart[g] <= tile
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (tstart[mid] <= tile) lo = mid; else hi = mid;
     }
-    const int g = __builtin_amdgcn_readfirstlane(lo);
+    g = __builtin_amdgcn_readfirstlane(lo);
     const int local = tile - __builtin_amdgcn_readfirstlane(tstart[g]);
-    const int mt = local / ntn, nt = local % ntn;
     const int64_t seg_lo = p.seg ? (int64_t)p.seg[g] : 0;
     const int64_t seg_hi = p.seg ? (int64_t)p.seg[g + 1] : p.M;
-    const int64_t m0 = seg_lo + (int64_t)mt * BM;
-    const int n0 = nt * NOUT;
-    const int rows_valid = (int)min<int64_t>(BM, seg_hi - m0);
+    // Within a group the tiles run in column groups of NG column tiles: for each
+    // column group, every row tile, and inside it the group's column tiles.  With
+    // NG = all columns this is plain row-major order.
+    const int mtc = (int)((seg_hi - seg_lo + BM - 1) / BM);
+    const int NG = (p.n_group > 0 && p.n_group < ntn) ? p.n_group : ntn;
+    const int cg = local / (mtc * NG);
+    const int l = local - cg * mtc * NG;
+    const int sz = min(NG, ntn - cg * NG);
+    const int mt = l / sz, nt = cg * NG + l % sz;
+    m0 = seg_lo + (int64_t)mt * BM;
+    n0 = nt * NOUT;
+    rows_valid = (int)min<int64_t>(BM, seg_hi - m0);
+  };
 
-    // Uniform (SGPR) tile bases; each lane adds a fixed 32-bit byte offset, so the
-    // direct-to-LDS loads use the scalar-base + vector-offset addressing form.
-    const char* Ab = reinterpret_cast<const char*>(Abase + m0 * K);
-    const char* Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)g * p.b_stride +
-                                                    (int64_t)n0 * K);
-    const char* Bub = (EPI == EPI_SWIGLU)
-        ? reinterpret_cast<const char*>(static_cast<const T*>(p.B1) + (int64_t)g * p.b_stride + (int64_t)n0 * K)
-        : nullptr;
-
-    // ---- per-thread source offsets (bytes, relative to the tile's bases) ----
-    // Load step i covers LDS rows [i*kRowsPerStep, (i+1)*kRowsPerStep); whether it
-    // reads A, gate or up is known at compile time.
-    uint32_t soff[CPT];
+  // Uniform (SGPR) tile bases plus a fixed 32-bit byte offset per lane and load
+  // step, so the direct-to-LDS loads use the scalar-base + vector-offset form.
+  const char* Ab = nullptr;
+  const char* Bgb = nullptr;
+  const char* Bub = nullptr;
+  uint32_t soff[CPT];
+  auto setup = [&]() {
+    Ab = reinterpret_cast<const char*>(Abase + m0 * K);
+    Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)g * p.b_stride + (int64_t)n0 * K);
+    if (EPI == EPI_SWIGLU)
+      Bub = reinterpret_cast<const char*>(static_cast<const T*>(p.B1) + (int64_t)g * p.b_stride + (int64_t)n0 * K);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
+      // load step i covers LDS rows [i*kRowsPerStep, (i+1)*kRowsPerStep); whether
+      // it reads A, gate or up is known at compile time
       const int byte = (i * NT + tid) * 16;
       const int row = byte / RB;
       const int lc = Cfg::swz(row, (byte % RB) / 16);
@@ -250,22 +275,80 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
       }
       soff[i] = ((uint32_t)r * (uint32_t)K + (uint32_t)(lc * EPC)) * (uint32_t)sizeof(T);
     }
-
-    auto load_stage = [&](int stage, int k0) {
-      const uint32_t lbase = lds_addr_of(smem) + stage * Cfg::kStageBytes + wave * 64 * 16;
-      const int64_t kb = (int64_t)k0 * (int64_t)sizeof(T);
+  };
+  auto load_stage = [&](int stage, int kt) {
+    const uint32_t lbase = lds_addr_of(smem) + stage * Cfg::kStageBytes + wave * 64 * 16;
+    const int64_t kb = (int64_t)kt * BK * (int64_t)sizeof(T);
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const int row0 = i * Cfg::kRowsPerStep;               // compile-time region of step i
-        const char* base;
-        if (row0 < BM) base = Ab;
-        else if (EPI == EPI_SWIGLU && row0 - BM >= BN / 2) base = Bub;
-        else base = Bgb;
-        lds_dma16(base + kb, soff[i], lbase + i * NT * 16);
-      }
-    };
+    for (int i = 0; i < CPT; ++i) {
+      const int row0 = i * Cfg::kRowsPerStep;
+      const char* base;
+      if (row0 < BM) base = Ab;
+      else if (EPI == EPI_SWIGLU && row0 - BM >= BN / 2) base = Bub;
+      else base = Bgb;
+      lds_dma16(base + kb, soff[i], lbase + i * NT * 16);
+    }
+  };
+  auto prologue = [&]() {
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) load_stage(s, s);
+  };
 
-    f32x16 acc[MI][NI];
+  // Row blocks past the end of a ragged row tile carry no output: their MFMAs and
+  // A-fragment reads are skipped (mi_live is wave-uniform).
+  int mi_live = MI;
+
+  // ---- MFMA operand fragments: one buffer per sub-step of a k-tile, read PD
+  //      sub-steps ahead of the MFMAs that use them -------------------------------
+  typename Op::Frag fa[KSUB][MI], fb[KSUB][NI];
+  auto read_frags = [&](int buf, int stage, int sub) {
+    const char* sA = smem + stage * Cfg::kStageBytes;
+    const char* sB = sA + BM * RB;
+    const int lc0 = sub * 2 * Cfg::CPL + (lane >> 5) * Cfg::CPL;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      if (mi >= mi_live) continue;
+      const int r = wm * Cfg::WTM + mi * 32 + (lane & 31);
+      if constexpr (Op::kReads == 1)
+        Op::load(fa[buf][mi], sA + r * RB + Cfg::swz(r, lc0) * 16);
+      else
+        Op::load(fa[buf][mi], sA + r * RB + Cfg::swz(r, lc0) * 16, sA + r * RB + Cfg::swz(r, lc0 + 1) * 16);
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      const int r = Cfg::b_row(wn, ni) + (lane & 31);
+      if constexpr (Op::kReads == 1)
+        Op::load(fb[buf][ni], sB + r * RB + Cfg::swz(r, lc0) * 16);
+      else
+        Op::load(fb[buf][ni], sB + r * RB + Cfg::swz(r, lc0) * 16, sB + r * RB + Cfg::swz(r, lc0 + 1) * 16);
+    }
+  };
+  f32x16 acc[MI][NI];
+  // B (weights) is the MFMA's first operand: each block comes out transposed, so a
+  // lane ends up holding 4 consecutive output columns of one row.
+  auto mma_all = [&](int buf) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+      if (mi < mi_live) {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) Op::mma(fb[buf][ni], fa[buf][mi], acc[mi][ni]);
+      }
+  };
+
+  // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b on XCD b % 8)
+  // and each XCD has its own L2.  Give the 32 workgroups of one XCD a contiguous
+  // run of the tile list in every round, so that the tiles resident on an XCD
+  // share their A rows (all column tiles of a row tile) and expert weights.
+  const int grid = gridDim.x;
+  int tile = blockIdx.x;
+  if (grid % kXcds == 0) tile = (blockIdx.x % kXcds) * (grid / kXcds) + blockIdx.x / kXcds;
+  if (tile >= total) return;
+  locate(tile);
+  setup();
+  prologue();
+
+  while (true) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -273,64 +356,66 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
 
+    mi_live = __builtin_amdgcn_readfirstlane(min(MI, max(0, (rows_valid - wm * Cfg::WTM + 31) / 32)));
+
+    // k-tile 0 has landed (this wave's copies; the barrier covers the others)
+    if (STAGES - 2 <= nk - 1) wait_vmcnt<(STAGES - 2) * CPT>();
+    else wait_vmcnt<0>();
+    block_barrier();
+    if (STAGES - 1 < nk) load_stage((STAGES - 1) % STAGES, STAGES - 1);
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-      if (s < nk) load_stage(s, s * BK);
+    for (int s = 0; s < PD; ++s) read_frags(s, 0, s);
 
     for (int kt = 0; kt < nk; ++kt) {
-      // this wave's copies for k-tile kt have landed; the barrier makes every
-      // wave's copies visible and tells all waves that stage (kt-1)%STAGES is free
-      if (kt + STAGES - 2 < nk) wait_vmcnt<(STAGES - 2) * CPT>();
-      else wait_vmcnt<0>();
-      block_barrier();
-      if (kt + STAGES - 1 < nk) load_stage((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK);
-
-      const char* sA = smem + (kt % STAGES) * Cfg::kStageBytes;
-      const char* sB = sA + BM * RB;
+      const int st = kt % STAGES;
 #pragma unroll
-      for (int s = 0; s < Cfg::kSub; ++s) {
-        typename Op::Frag af[MI], bfr[NI];
-        const int lc0 = s * 2 * Cfg::CPL + (lane >> 5) * Cfg::CPL;
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-          const int r = wm * Cfg::WTM + mi * 32 + (lane & 31);
-          if constexpr (Op::kReads == 1)
-            Op::load(af[mi], sA + r * RB + Cfg::swz(r, lc0) * 16);
-          else
-            Op::load(af[mi], sA + r * RB + Cfg::swz(r, lc0) * 16, sA + r * RB + Cfg::swz(r, lc0 + 1) * 16);
+      for (int s = 0; s < KSUB; ++s) {
+        if (s + PD < KSUB) {
+          read_frags(s + PD, st, s + PD);
+        } else if (kt + 1 < nk) {
+          if (s + PD == KSUB) {
+            // every LDS read of stage st has been issued: wait for them, and for
+            // k-tile kt+1 to land, then recycle stage st for k-tile kt+STAGES
+            wait_lgkmcnt0();
+            if (kt + STAGES - 1 <= nk - 1) wait_vmcnt<(STAGES - 2) * CPT>();
+            else wait_vmcnt<0>();
+            block_barrier();
+            if (kt + STAGES < nk) load_stage(st, kt + STAGES);
+          }
+          read_frags(s + PD - KSUB, (kt + 1) % STAGES, s + PD - KSUB);
         }
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int r = Cfg::b_row(wn, ni) + (lane & 31);
-          if constexpr (Op::kReads == 1)
-            Op::load(bfr[ni], sB + r * RB + Cfg::swz(r, lc0) * 16);
-          else
-            Op::load(bfr[ni], sB + r * RB + Cfg::swz(r, lc0) * 16, sB + r * RB + Cfg::swz(r, lc0 + 1) * 16);
-        }
-        // B (weights) as the MFMA's first operand: the block comes out transposed,
-        // so each lane ends up with 4 consecutive output columns of one row.
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) Op::mma(bfr[ni], af[mi], acc[mi][ni]);
+        mma_all(s);
       }
     }
-    block_barrier();  // every wave is done with LDS before the next tile's copies
+
+    // this tile's LDS reads are done everywhere: start the next tile's copies, then
+    // store this tile from registers while they are in flight
+    wait_lgkmcnt0();
+    block_barrier();
+    const int64_t em0 = m0;
+    const int en0 = n0, erows = rows_valid;
+    tile += grid;
+    const bool more = tile < total;
+    if (more) {
+      locate(tile);
+      setup();
+      prologue();
+    }
 
     // ---- epilogue.  Block (mi, ni): lane holds output row (lane % 32) and the
-    //      columns 8*q + 4*(lane/32) + i in acc[4*q + i], q, i = 0..3 ------------
+    //      columns 8*q + 4*(lane/32) + i in acc[4*q + i], q, i = 0..3 -----------
     const int h4 = 4 * (lane >> 5);
     if constexpr (EPI == EPI_F32_BIAS) {
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         const int r = wm * Cfg::WTM + mi * 32 + (lane & 31);
-        if (r >= rows_valid) continue;
-        float* crow = static_cast<float*>(p.C) + (m0 + r) * (int64_t)p.N;
+        if (r >= erows) continue;
+        float* crow = static_cast<float*>(p.C) + (em0 + r) * (int64_t)p.N;
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int col = n0 + wn * Cfg::WTN + ni * 32 + 8 * q + h4;
+            const int col = en0 + wn * Cfg::WTN + ni * 32 + 8 * q + h4;
             if ((p.N & 3) == 0) {
               if (col < p.N) {
                 f32x4 v;
@@ -351,13 +436,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         const int r = wm * Cfg::WTM + mi * 32 + (lane & 31);
-        if (r >= rows_valid) continue;
-        T* crow = static_cast<T*>(p.C) + (m0 + r) * (int64_t)p.N;
+        if (r >= erows) continue;
+        T* crow = static_cast<T*>(p.C) + (em0 + r) * (int64_t)p.N;
 #pragma unroll
         for (int ni = 0; ni < NO; ++ni)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int col = n0 + wn * CW + ni * 32 + 8 * q + h4;
+            const int col = en0 + wn * CW + ni * 32 + 8 * q + h4;
             if (col < p.N) {
               float v[4];
 #pragma unroll
@@ -375,6 +460,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
           }
       }
     }
+    if (!more) break;
   }
 }
 

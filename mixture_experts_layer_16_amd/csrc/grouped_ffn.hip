@@ -20,7 +20,13 @@ namespace moe {
 
 namespace {
 
-template <typename T, int BK>
+// Column tiles per group in the tile order (0 = a row tile's columns all together).
+constexpr int kGateUpColumnGroup = 0;
+constexpr int kDownColumnGroup = 0;
+
+// Tile configuration: 256 x 256 output tiles, BK-deep k-slices, STAGES-deep LDS
+// ring, WM x WN wavefronts, MFMA operands read PD 16-k sub-steps ahead.
+template <typename T, int BK, int STAGES, int WM, int WN, int PD>
 void run(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm, const int32_t* offsets,
          const void* w_gate, const void* w_up, const void* w_down, void* y_perm, void* h, int num_cu,
          hipStream_t stream) {
@@ -36,7 +42,9 @@ void run(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm, con
   gu.K = (int32_t)d;
   gu.C = h;
   gu.bias = nullptr;
-  hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, 2, 2, 2, EPI_SWIGLU>), dim3(num_cu), dim3(256), 0,
+  gu.n_group = kGateUpColumnGroup;
+  hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, WM, WN, STAGES, EPI_SWIGLU, PD>), dim3(num_cu),
+                     dim3(WM * WN * 64), 0,
                      stream, gu);
 
   GemmArgs dn{};
@@ -51,7 +59,9 @@ void run(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm, con
   dn.K = (int32_t)F;
   dn.C = y_perm;
   dn.bias = nullptr;
-  hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, 2, 2, 2, EPI_STORE>), dim3(num_cu), dim3(256), 0,
+  dn.n_group = kDownColumnGroup;
+  hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, WM, WN, STAGES, EPI_STORE, PD>), dim3(num_cu),
+                     dim3(WM * WN * 64), 0,
                      stream, dn);
 }
 
@@ -61,9 +71,9 @@ hipError_t launch_grouped_ffn(int dtype, int64_t n_max, int64_t d, int64_t E, in
                               const int32_t* offsets, const void* w_gate, const void* w_up, const void* w_down,
                               void* y_perm, void* h, int num_cu, hipStream_t stream) {
   if (dtype == 1)
-    run<bf16, 64>(n_max, d, E, F, x_perm, offsets, w_gate, w_up, w_down, y_perm, h, num_cu, stream);
+    run<bf16, 64, 2, 4, 2, 1>(n_max, d, E, F, x_perm, offsets, w_gate, w_up, w_down, y_perm, h, num_cu, stream);
   else
-    run<float, 32>(n_max, d, E, F, x_perm, offsets, w_gate, w_up, w_down, y_perm, h, num_cu, stream);
+    run<float, 32, 2, 4, 2, 1>(n_max, d, E, F, x_perm, offsets, w_gate, w_up, w_down, y_perm, h, num_cu, stream);
   return hipGetLastError();
 }
 

@@ -137,11 +137,12 @@ hipError_t launch_router_gemm(int dtype, int64_t T, int64_t d, int64_t E, const 
   a.K = (int32_t)d;
   a.C = logits;
   a.bias = bias;
-  const dim3 grid((unsigned)num_cu), block(256);
+  a.n_group = 0;
+  const dim3 grid((unsigned)num_cu), block(512);
   if (dtype == 1)
-    hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, 64, 2, 2, 2, EPI_F32_BIAS>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, 64, 4, 2, 2, EPI_F32_BIAS>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_kernel<float, 256, 256, 32, 2, 2, 2, EPI_F32_BIAS>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((grouped_gemm_kernel<float, 256, 256, 32, 4, 2, 2, EPI_F32_BIAS>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
