@@ -37,7 +37,49 @@ def parse():
     ap.add_argument("--workload", default="page_seq64k_skewed")
     ap.add_argument("--cpu-tokens", type=int, default=512,
                     help="tokens of the workload the CPU oracle runs on (0 = skip)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run one 1 GiB device copy, then one grouped FFN call, and exit "
+                         "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
     return ap.parse_args()
+
+
+# HBM traffic of one grouped-FFN call (gate/up + down launches) at 65,536 tokens
+# of the page shape, from rocprofv3 FETCH_SIZE and WRITE_SIZE runs of
+# `bench.py --traffic-probe`, each scaled by the same counter's reading for a
+# 1 GiB device copy.  Valid only for the kernel sources it was measured on.
+TRAFFIC = None
+KERNEL_SOURCES = ["mixture_experts_layer_16_amd/csrc/gemm_tile.h", "mixture_experts_layer_16_amd/csrc/grouped_ffn.hip",
+                  "mixture_experts_layer_16_amd/csrc/common.h"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_probe(torch, B, W, wl):
+    """One plain 1 GiB copy (the counters' calibration) and one grouped FFN call."""
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    inp = W.make_inputs(wl, device="cuda:0")
+    if inp["w_router"] is not None:
+        ids, w, _ = B.moe_route(inp["x"], inp["w_router"], wl.k, bias=inp["bias"], want_logits=False)
+    else:
+        ids, w = inp["topk_ids"], inp["topk_w"]
+    off, rt, sr, _ = B.moe_permute(inp["x"], ids, wl.E, copy_rows=False)
+    yp = torch.empty(rt.numel(), wl.d, dtype=inp["x"].dtype, device="cuda:0")
+    torch.cuda.synchronize()
+    B.moe_grouped_ffn(inp["x"], off, inp["w_gate"], inp["w_up"], inp["w_down"], y_perm=yp, a_rows=rt)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_probe": wl.name, "kernel_source_hash": kernel_source_hash()}), flush=True)
 
 
 def stage_pass(torch, B, inp, wl, steps):
@@ -55,10 +97,10 @@ def stage_pass(torch, B, inp, wl, steps):
             ev[i].record()
         else:
             ids, w = inp["topk_ids"], inp["topk_w"]
-        off, rt, sr, xp = B.moe_permute(inp["x"], ids, wl.E)
+        off, rt, sr, _ = B.moe_permute(inp["x"], ids, wl.E, copy_rows=False)
         i += 1
         ev[i].record()
-        yp = B.moe_grouped_ffn(xp, off, inp["w_gate"], inp["w_up"], inp["w_down"], y_perm=xp)
+        yp = B.moe_grouped_ffn(inp["x"], off, inp["w_gate"], inp["w_up"], inp["w_down"], a_rows=rt)
         i += 1
         ev[i].record()
         B.moe_combine(yp, sr, w)
@@ -67,7 +109,7 @@ def stage_pass(torch, B, inp, wl, steps):
         torch.cuda.synchronize()
         for j, n in enumerate(names):
             acc[n] += ev[j].elapsed_time(ev[j + 1])
-        del off, rt, sr, xp, yp
+        del off, rt, sr, yp
     return {n: v / steps for n, v in acc.items()}
 
 
@@ -115,6 +157,9 @@ def main():
 
     wl = W.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    if args.traffic_probe:
+        traffic_probe(torch, B, W, wl)
+        return
     inp = W.make_inputs(wl, device="cuda:0")
     L = B.LayerForward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"], inp["w_down"], wl.k,
                        topk_ids=inp.get("topk_ids"), topk_w=inp.get("topk_w"))
@@ -138,7 +183,10 @@ def main():
     ffn_tflops = wl.expert_flops() / (ffn_ms / 1e3) / 1e12
     total_tflops = (wl.expert_flops() + wl.router_flops()) / (ms / 1e3) / 1e12
     es = 2 if wl.dtype == torch.bfloat16 else 4
-    perm_bytes = wl.T * wl.d * es + wl.N * wl.d * es + wl.T * wl.k * 4 * 3
+    traffic = None
+    if TRAFFIC and TRAFFIC["kernel_source_hash"] == kernel_source_hash() and TRAFFIC["workload"] == wl.name:
+        traffic = TRAFFIC["bytes"]
+    perm_bytes = wl.T * wl.k * 4 * 3                  # indices only: ids read, slot_row and row_token written
     comb_bytes = wl.N * wl.d * es + wl.T * wl.d * es + wl.T * wl.k * 8
 
     out = {
@@ -149,7 +197,7 @@ def main():
         "config": {"workload": wl.name, "tokens": wl.T, "hidden": wl.d, "experts": wl.E, "top_k": wl.k,
                    "expert_hidden": wl.F, "routing": wl.routing, "slots": wl.N},
         "roofline": {"bound": "mfma", "achieved": round(ffn_tflops, 1), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(ffn_tflops / peak, 4), "traffic": None,
+                     "frac": round(ffn_tflops / peak, 4), "traffic": traffic,
                      "kernel": "grouped SwiGLU FFN (gate/up + down GEMM launches)",
                      "flops_per_launch": wl.expert_flops(), "ms_per_launch": round(ffn_ms, 4)},
         "tflops_layer": round(total_tflops, 1),

@@ -91,7 +91,9 @@ moe_status moe_route(int64_t T, int64_t d, int64_t E, int64_t k, moe_dtype dtype
  *   row_token  [T*k]   int32     out: row r copies token row_token[r]; rows of one
  *                                 expert are in ascending token order (first N written)
  *   slot_row   [T*k]   int32     out: row of slot (t,j), or -1 for a skipped slot
- *   x_perm     [T*k,d] dtype     out: x_perm[r] = x[row_token[r]] (first N rows written)
+ *   x_perm     [T*k,d] dtype     out: x_perm[r] = x[row_token[r]] (first N rows written);
+ *                                 NULL: only the indices are produced (the grouped FFN
+ *                                 can read x in place through row_token)
  *   ws                           workspace: ceil(T/256)*E*4 bytes
  */
 moe_status moe_permute(int64_t T, int64_t d, int64_t E, int64_t k, moe_dtype dtype,
@@ -101,22 +103,31 @@ moe_status moe_permute(int64_t T, int64_t d, int64_t E, int64_t k, moe_dtype dty
 
 /*
  * moe_grouped_ffn: the SwiGLU FFN of every expert over its own rows.
- *   n_max              capacity (rows) of x_perm and y_perm; offsets[E] <= n_max
- *                       is the caller's promise (the row count is read on the
- *                       device; nothing is copied back)
- *   x_perm   [n_max,d] dtype   rows grouped by expert
+ *   n_max              capacity (rows) of y_perm (and of x_in without a_rows);
+ *                       offsets[E] <= n_max is the caller's promise (the row count
+ *                       is read on the device; nothing is copied back)
+ *   x_in               the FFN's input rows, one of:
+ *                        a_rows == NULL: x_perm [n_max,d], rows grouped by expert;
+ *                        a_rows != NULL: the token matrix x [n_in,d]; row r of the
+ *                          FFN input is x[a_rows[r]] (a_rows = row_token from
+ *                          moe_permute), read in place without a permuted copy.
+ *                          Requires n_in*d*sizeof(dtype) < 2^32 and 0 <= a_rows[r] < n_in.
+ *   n_in               rows of x_in when a_rows != NULL (ignored otherwise)
+ *   a_rows   [n_max]   int32   NULL or the gather map described above
  *   offsets  [E+1]     int32   device array as written by moe_permute; empty experts allowed
  *   w_gate   [E,F,d]   dtype
  *   w_up     [E,F,d]   dtype
  *   w_down   [E,d,F]   dtype
- *   y_perm   [n_max,d] dtype   out: y_perm[r] = W_d[e](silu(W_g[e] x_perm[r]) * (W_u[e] x_perm[r]))
- *                               for the expert e owning row r (first offsets[E] rows)
+ *   y_perm   [n_max,d] dtype   out: y_perm[r] = W_d[e](silu(W_g[e] v_r) * (W_u[e] v_r)) for
+ *                               input row v_r of expert e (first offsets[E] rows); may be
+ *                               the same buffer as x_perm
  *   ws                          workspace: n_max*F*sizeof(dtype) bytes (the hidden activations h)
  */
 moe_status moe_grouped_ffn(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_dtype dtype,
-                           const void* x_perm, const int32_t* offsets,
-                           const void* w_gate, const void* w_up, const void* w_down,
-                           void* y_perm, void* ws, size_t* ws_bytes, void* stream);
+                           const void* x_in, int64_t n_in, const int32_t* a_rows,
+                           const int32_t* offsets, const void* w_gate, const void* w_up,
+                           const void* w_down, void* y_perm, void* ws, size_t* ws_bytes,
+                           void* stream);
 
 /*
  * moe_combine: weighted un-permute.

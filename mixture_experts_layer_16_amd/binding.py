@@ -34,7 +34,7 @@ _i64, _int, _vp, _szp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.PO
 _SIGS = {
     "moe_route": [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp],
     "moe_permute": [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp],
-    "moe_grouped_ffn": [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp],
+    "moe_grouped_ffn": [_i64, _i64, _i64, _i64, _int, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp],
     "moe_combine": [_i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp],
     "moe_layer_forward": [_i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                           _vp, _vp, _szp, _vp],
@@ -108,15 +108,16 @@ def moe_route(x, w_router, k: int, bias=None, want_logits: bool = True):
     return ids, w, logits
 
 
-def moe_permute(x, topk_ids, num_experts: int):
-    """Returns (offsets [E+1], row_token [T*k], slot_row [T,k], x_perm [T*k, d])."""
+def moe_permute(x, topk_ids, num_experts: int, copy_rows: bool = True):
+    """Returns (offsets [E+1], row_token [T*k], slot_row [T,k], x_perm [T*k, d] | None).
+    copy_rows=False produces only the indices (x_perm is None)."""
     T, d = x.shape
     k = topk_ids.shape[1]
     dev = x.device
     offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
     row_token = torch.empty(T * k, dtype=torch.int32, device=dev)
     slot_row = torch.empty(T, k, dtype=torch.int32, device=dev)
-    x_perm = torch.empty(T * k, d, dtype=x.dtype, device=dev)
+    x_perm = torch.empty(T * k, d, dtype=x.dtype, device=dev) if copy_rows else None
     head = (T, d, num_experts, k, dtype_code(x.dtype), _p(x), _p(topk_ids), _p(offsets), _p(row_token),
             _p(slot_row), _p(x_perm))
     ws = _ws(_query("moe_permute", *head), dev)
@@ -125,15 +126,21 @@ def moe_permute(x, topk_ids, num_experts: int):
     return offsets, row_token, slot_row, x_perm
 
 
-def moe_grouped_ffn(x_perm, offsets, w_gate, w_up, w_down, y_perm=None):
-    """y_perm [n_max, d]: the SwiGLU FFN of each expert over its rows."""
-    n_max, d = x_perm.shape
+def moe_grouped_ffn(x_in, offsets, w_gate, w_up, w_down, y_perm=None, a_rows=None, n_max=None):
+    """y_perm [n_max, d]: the SwiGLU FFN of each expert over its rows.  Without
+    a_rows, x_in is x_perm (rows grouped by expert); with a_rows (row_token from
+    moe_permute), x_in is the token matrix x read in place."""
+    d = x_in.shape[1]
+    if a_rows is None:
+        n_max, n_in = x_in.shape[0], 0
+    else:
+        n_max, n_in = (a_rows.numel() if n_max is None else n_max), x_in.shape[0]
     E, F, _ = w_gate.shape
-    dev = x_perm.device
+    dev = x_in.device
     if y_perm is None:
-        y_perm = torch.empty_like(x_perm)
-    head = (n_max, d, E, F, dtype_code(x_perm.dtype), _p(x_perm), _p(offsets), _p(w_gate), _p(w_up), _p(w_down),
-            _p(y_perm))
+        y_perm = torch.empty(n_max, d, dtype=x_in.dtype, device=dev)
+    head = (n_max, d, E, F, dtype_code(x_in.dtype), _p(x_in), n_in, _p(a_rows), _p(offsets), _p(w_gate), _p(w_up),
+            _p(w_down), _p(y_perm))
     ws = _ws(_query("moe_grouped_ffn", *head), dev)
     n = ctypes.c_size_t(ws.numel())
     _check("moe_grouped_ffn", lib().moe_grouped_ffn(*head, _p(ws), ctypes.byref(n), _stream(dev)))

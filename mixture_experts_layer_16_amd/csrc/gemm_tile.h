@@ -30,6 +30,8 @@ constexpr int kXcds = 8;   // accelerator complex dies of an MI355X, one L2 each
 
 struct GemmArgs {
   const void* A;          // [rows, K]; group g owns rows seg[g] .. seg[g+1]-1
+  const int32_t* a_rows;  // nullptr, or a gather map: logical row r is row a_rows[r] of A
+                          // (A's byte size must then stay below 4 GiB)
   const void* B0;         // group g: B0 + g * b_stride elements, [N, K]
   const void* B1;         // EPI_SWIGLU: the "up" matrix, same layout as B0
   int64_t b_stride;       // elements between two groups' B matrices
@@ -41,6 +43,7 @@ struct GemmArgs {
   void* C;                // [rows, N] output (row stride N)
   const float* bias;      // EPI_F32_BIAS: [N] or nullptr
   int32_t n_group;        // tile order: column tiles per group (<= 0: all columns of a row tile)
+  int32_t m_chunk;        // tile order: row tiles per chunk (<= 0: all row tiles of a group)
 };
 
 // Per element type: how one wave multiplies a 32x32 block over 16 k values.
@@ -232,15 +235,22 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     const int local = tile - __builtin_amdgcn_readfirstlane(tstart[g]);
     const int64_t seg_lo = p.seg ? (int64_t)p.seg[g] : 0;
     const int64_t seg_hi = p.seg ? (int64_t)p.seg[g + 1] : p.M;
-    // Within a group the tiles run in column groups of NG column tiles: for each
-    // column group, every row tile, and inside it the group's column tiles.  With
-    // NG = all columns this is plain row-major order.
+    // Within a group the tiles run in chunks of SM row tiles; inside a chunk, in
+    // column groups of NG column tiles; inside a column group, row tile by row
+    // tile.  Consecutive tiles then share A rows (same row tile) and B columns
+    // (same column group), and a chunk's A rows stay hot while its column groups
+    // go by.
     const int mtc = (int)((seg_hi - seg_lo + BM - 1) / BM);
+    const int SM = (p.m_chunk > 0 && p.m_chunk < mtc) ? p.m_chunk : mtc;
     const int NG = (p.n_group > 0 && p.n_group < ntn) ? p.n_group : ntn;
-    const int cg = local / (mtc * NG);
-    const int l = local - cg * mtc * NG;
+    const int ch = local / (SM * ntn);
+    const int base_m = ch * SM;
+    const int sm = min(SM, mtc - base_m);
+    const int l = local - ch * SM * ntn;
+    const int cg = l / (sm * NG);
+    const int l2 = l - cg * sm * NG;
     const int sz = min(NG, ntn - cg * NG);
-    const int mt = l / sz, nt = cg * NG + l % sz;
+    const int mt = base_m + l2 / sz, nt = cg * NG + l2 % sz;
     m0 = seg_lo + (int64_t)mt * BM;
     n0 = nt * NOUT;
     rows_valid = (int)min<int64_t>(BM, seg_hi - m0);
@@ -253,7 +263,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   const char* Bub = nullptr;
   uint32_t soff[CPT];
   auto setup = [&]() {
-    Ab = reinterpret_cast<const char*>(Abase + m0 * K);
+    Ab = reinterpret_cast<const char*>(p.a_rows ? Abase : Abase + m0 * K);
     Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)g * p.b_stride + (int64_t)n0 * K);
     if (EPI == EPI_SWIGLU)
       Bub = reinterpret_cast<const char*>(static_cast<const T*>(p.B1) + (int64_t)g * p.b_stride + (int64_t)n0 * K);
@@ -267,6 +277,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
       int r;
       if (row < BM) {
         r = min(row, rows_valid - 1);                         // rows past the segment: any valid row
+        if (p.a_rows) r = p.a_rows[m0 + r];                   // gathered row of A
       } else {
         const int br = row - BM;
         const int half = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
@@ -337,13 +348,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   };
 
   // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b on XCD b % 8)
-  // and each XCD has its own L2.  Give the 32 workgroups of one XCD a contiguous
-  // run of the tile list in every round, so that the tiles resident on an XCD
-  // share their A rows (all column tiles of a row tile) and expert weights.
+  // and each XCD has its own L2.  Give the workgroups of one XCD a contiguous run
+  // of the tile list in every round, so that the tiles resident on an XCD share
+  // their A rows (the column tiles of a row tile) and expert weights.
   const int grid = gridDim.x;
   int tile = blockIdx.x;
+  const int step = grid, end = total;
   if (grid % kXcds == 0) tile = (blockIdx.x % kXcds) * (grid / kXcds) + blockIdx.x / kXcds;
-  if (tile >= total) return;
+  if (tile >= end) return;
   locate(tile);
   setup();
   prologue();
@@ -394,8 +406,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     block_barrier();
     const int64_t em0 = m0;
     const int en0 = n0, erows = rows_valid;
-    tile += grid;
-    const bool more = tile < total;
+    tile += step;
+    const bool more = tile < end;
     if (more) {
       locate(tile);
       setup();

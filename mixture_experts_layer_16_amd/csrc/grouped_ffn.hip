@@ -8,7 +8,9 @@
 //
 // Two persistent launches of the grouped GEMM template:
 //   gate/up: one A tile against the gate AND the up tile of the same columns,
-//            SwiGLU in registers, h stored once (never the two halves);
+//            SwiGLU in registers, h stored once (never the two halves); the A
+//            rows are either x_perm's rows or, with a gather map, token rows of
+//            x read in place (no permuted copy of x is ever written);
 //   down:    y_perm = h W_d^T.
 // Row counts per expert are read on the device from the offsets; experts with
 // no rows own no tile.
@@ -20,18 +22,23 @@ namespace moe {
 
 namespace {
 
-// Column tiles per group in the tile order (0 = a row tile's columns all together).
+// Tile order inside an expert: chunks of row tiles, column groups inside a chunk
+// (0 = no chunking / all columns together).
+constexpr int kGateUpRowChunk = 0;
 constexpr int kGateUpColumnGroup = 0;
+constexpr int kDownRowChunk = 0;
 constexpr int kDownColumnGroup = 0;
 
 // Tile configuration: 256 x 256 output tiles, BK-deep k-slices, STAGES-deep LDS
 // ring, WM x WN wavefronts, MFMA operands read PD 16-k sub-steps ahead.
 template <typename T, int BK, int STAGES, int WM, int WN, int PD>
-void run(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm, const int32_t* offsets,
+void run(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm, const int32_t* a_rows,
+         const int32_t* offsets,
          const void* w_gate, const void* w_up, const void* w_down, void* y_perm, void* h, int num_cu,
          hipStream_t stream) {
   GemmArgs gu{};
   gu.A = x_perm;
+  gu.a_rows = a_rows;
   gu.B0 = w_gate;
   gu.B1 = w_up;
   gu.b_stride = F * d;
@@ -43,12 +50,14 @@ void run(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm, con
   gu.C = h;
   gu.bias = nullptr;
   gu.n_group = kGateUpColumnGroup;
+  gu.m_chunk = kGateUpRowChunk;
   hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, WM, WN, STAGES, EPI_SWIGLU, PD>), dim3(num_cu),
                      dim3(WM * WN * 64), 0,
                      stream, gu);
 
   GemmArgs dn{};
   dn.A = h;
+  dn.a_rows = nullptr;
   dn.B0 = w_down;
   dn.B1 = nullptr;
   dn.b_stride = d * F;
@@ -60,6 +69,7 @@ void run(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm, con
   dn.C = y_perm;
   dn.bias = nullptr;
   dn.n_group = kDownColumnGroup;
+  dn.m_chunk = kDownRowChunk;
   hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, WM, WN, STAGES, EPI_STORE, PD>), dim3(num_cu),
                      dim3(WM * WN * 64), 0,
                      stream, dn);
@@ -68,12 +78,12 @@ void run(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm, con
 }  // namespace
 
 hipError_t launch_grouped_ffn(int dtype, int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm,
-                              const int32_t* offsets, const void* w_gate, const void* w_up, const void* w_down,
+                              const int32_t* a_rows, const int32_t* offsets, const void* w_gate, const void* w_up, const void* w_down,
                               void* y_perm, void* h, int num_cu, hipStream_t stream) {
   if (dtype == 1)
-    run<bf16, 64, 2, 4, 2, 1>(n_max, d, E, F, x_perm, offsets, w_gate, w_up, w_down, y_perm, h, num_cu, stream);
+    run<bf16, 64, 2, 4, 2, 1>(n_max, d, E, F, x_perm, a_rows, offsets, w_gate, w_up, w_down, y_perm, h, num_cu, stream);
   else
-    run<float, 32, 2, 4, 2, 1>(n_max, d, E, F, x_perm, offsets, w_gate, w_up, w_down, y_perm, h, num_cu, stream);
+    run<float, 32, 2, 4, 2, 1>(n_max, d, E, F, x_perm, a_rows, offsets, w_gate, w_up, w_down, y_perm, h, num_cu, stream);
   return hipGetLastError();
 }
 

@@ -17,16 +17,18 @@ hipError_t launch_router_gemm(int dtype, int64_t T, int64_t d, int64_t E, const 
 hipError_t launch_topk(int64_t T, int64_t E, int64_t k, const float* logits, int32_t* ids,
                        float* w, hipStream_t stream);
 
-// Permutation: counts per 256-token block, scan, stable scatter + row copy.
+// Permutation: counts per 256-token block, scan, stable scatter + row copy
+// (x_perm == nullptr: indices only).
 hipError_t launch_permute(int dtype, int64_t T, int64_t d, int64_t E, int64_t k, const void* x,
                           const int32_t* ids, int32_t* offsets, int32_t* row_token,
                           int32_t* slot_row, void* x_perm, int32_t* block_counts,
                           hipStream_t stream);
 constexpr int kPermuteBlockTokens = 256;
 
-// Grouped SwiGLU FFN: h = silu(x_perm W_g^T) * (x_perm W_u^T); y_perm = h W_d^T.
+// Grouped SwiGLU FFN: h = silu(X W_g^T) * (X W_u^T); y_perm = h W_d^T, where row r
+// of X is x_perm[r], or x[a_rows[r]] when a gather map is given.
 hipError_t launch_grouped_ffn(int dtype, int64_t n_max, int64_t d, int64_t E, int64_t F,
-                              const void* x_perm, const int32_t* offsets, const void* w_gate,
+                              const void* x_perm, const int32_t* a_rows, const int32_t* offsets, const void* w_gate,
                               const void* w_up, const void* w_down, void* y_perm, void* h,
                               int num_cu, hipStream_t stream);
 

@@ -145,31 +145,37 @@ moe_status moe_permute(int64_t T, int64_t d, int64_t E, int64_t k, moe_dtype dty
     *ws_bytes = need;
     return MOE_OK;
   }
-  if (!ok16(x) || !ok4(topk_ids) || !ok4(offsets) || !ok4(row_token) || !ok4(slot_row) || !ok16(x_perm))
+  if (!ok16(x) || !ok4(topk_ids) || !ok4(offsets) || !ok4(row_token) || !ok4(slot_row) || !opt16(x_perm))
     return MOE_ERR_INVALID_ARG;
   if (workspace_step(ws, ws_bytes, need, &st)) return st;
   return hip_status(moe::launch_permute(dtype, T, d, E, k, x, topk_ids, offsets, row_token, slot_row, x_perm,
                                         static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream)));
 }
 
-moe_status moe_grouped_ffn(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_dtype dtype, const void* x_perm,
-                           const int32_t* offsets, const void* w_gate, const void* w_up, const void* w_down,
-                           void* y_perm, void* ws, size_t* ws_bytes, void* stream) {
+moe_status moe_grouped_ffn(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_dtype dtype, const void* x_in,
+                           int64_t n_in, const int32_t* a_rows, const int32_t* offsets, const void* w_gate,
+                           const void* w_up, const void* w_down, void* y_perm, void* ws, size_t* ws_bytes,
+                           void* stream) {
   moe_status st = check_ffn_dims(n_max, d, E, F);
   if (st != MOE_OK) return st;
   if ((st = check_dtype(dtype)) != MOE_OK) return st;
+  if (a_rows != nullptr) {
+    if (n_in <= 0) return MOE_ERR_INVALID_ARG;
+    if ((uint64_t)n_in * (uint64_t)d * elem_size(dtype) >= (uint64_t(1) << 32)) return MOE_ERR_UNSUPPORTED;
+  }
   const size_t need = round_up((size_t)n_max * (size_t)F * elem_size(dtype));
   if (ws == nullptr && ws_bytes != nullptr) {
     *ws_bytes = need;
     return MOE_OK;
   }
-  if (!ok16(x_perm) || !ok4(offsets) || !ok16(w_gate) || !ok16(w_up) || !ok16(w_down) || !ok16(y_perm))
+  if (!ok16(x_in) || !opt4(a_rows) || !ok4(offsets) || !ok16(w_gate) || !ok16(w_up) || !ok16(w_down) ||
+      !ok16(y_perm))
     return MOE_ERR_INVALID_ARG;
   if (workspace_step(ws, ws_bytes, need, &st)) return st;
   int ncu = 0;
   if ((st = num_cu(&ncu)) != MOE_OK) return st;
-  return hip_status(moe::launch_grouped_ffn(dtype, n_max, d, E, F, x_perm, offsets, w_gate, w_up, w_down, y_perm,
-                                            ws, ncu, static_cast<hipStream_t>(stream)));
+  return hip_status(moe::launch_grouped_ffn(dtype, n_max, d, E, F, x_in, a_rows, offsets, w_gate, w_up, w_down,
+                                            y_perm, ws, ncu, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_combine(int64_t T, int64_t d, int64_t k, moe_dtype dtype, const void* y_perm,
@@ -205,7 +211,7 @@ moe_status moe_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
   int32_t* row_token = static_cast<int32_t*>(c.take(slots * 4));
   int32_t* slot_row = static_cast<int32_t*>(c.take(slots * 4));
   int32_t* counts = static_cast<int32_t*>(c.take(permute_ws(T, E)));
-  void* x_perm = c.take(slots * (size_t)d * es);   // later reused for y_perm
+  void* y_perm = c.take(slots * (size_t)d * es);   // also holds x_perm when x is not read in place
   void* h = c.take(slots * (size_t)F * es);
   const size_t need = c.used;
 
@@ -231,15 +237,19 @@ moe_status moe_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
       return st;
     if ((st = hip_status(moe::launch_topk(T, E, k, logits, ids, w, s))) != MOE_OK) return st;
   }
-  if ((st = hip_status(moe::launch_permute(dtype, T, d, E, k, x, ids, offsets, row_token, slot_row, x_perm, counts,
-                                           s))) != MOE_OK)
+  // The gate/up GEMM reads token rows of x in place through row_token (no permuted
+  // copy of x) whenever x's byte size fits the kernel's 32-bit row offsets.
+  // Otherwise x is first copied to x_perm in y_perm's buffer; the down GEMM then
+  // overwrites it, after the gate/up GEMM (same stream) has finished reading it.
+  const bool in_place = (uint64_t)T * (uint64_t)d * es < (uint64_t(1) << 32);
+  if ((st = hip_status(moe::launch_permute(dtype, T, d, E, k, x, ids, offsets, row_token, slot_row,
+                                           in_place ? nullptr : y_perm, counts, s))) != MOE_OK)
     return st;
-  // y_perm overwrites x_perm: the down GEMM runs after the gate/up GEMM has
-  // finished reading x_perm (same stream).
-  if ((st = hip_status(moe::launch_grouped_ffn(dtype, (int64_t)slots, d, E, F, x_perm, offsets, w_gate, w_up, w_down,
-                                               x_perm, h, ncu, s))) != MOE_OK)
+  if ((st = hip_status(moe::launch_grouped_ffn(dtype, (int64_t)slots, d, E, F, in_place ? x : y_perm,
+                                               in_place ? row_token : nullptr, offsets, w_gate, w_up, w_down,
+                                               y_perm, h, ncu, s))) != MOE_OK)
     return st;
-  return hip_status(moe::launch_combine(dtype, T, d, k, x_perm, slot_row, w, y, s));
+  return hip_status(moe::launch_combine(dtype, T, d, k, y_perm, slot_row, w, y, s));
 }
 
 }  // extern "C"

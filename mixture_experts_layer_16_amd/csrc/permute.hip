@@ -11,8 +11,8 @@
 //               a slot's rank among its block's rows of that expert is the
 //               popcount of the bits of lower tokens, so
 //               row = offsets[e] + block_prefix[b][e] + rank;
-//               the block then copies each token's row to its k destinations
-//               with 16-byte vector loads and stores.
+//               then (unless only indices are wanted) the block copies each
+//               token's row to its k destinations with 16-byte vectors.
 // No global atomics: two runs give identical bits.  A token's ids must be
 // distinct; a negative id (or one >= E) marks a slot that is skipped.
 #include "common.h"
@@ -105,7 +105,25 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const T* __restric
   }
   __syncthreads();
 
-  // each wavefront handles tokens wave, wave+4, ...; lanes copy 16-byte chunks
+  // indices: one thread per slot
+  for (int64_t s = s0 + threadIdx.x; s < s1; s += 256) {
+    const int e = ids[s];
+    const int t = (int)(s / k);
+    int row = -1;
+    if (e >= 0 && e < E) {
+      const int tl = t - t0;
+      const uint32_t* w = bits + e * WPB;
+      int rank = __popc(w[tl >> 5] & ((1u << (tl & 31)) - 1u));
+      for (int q = 0; q < (tl >> 5); ++q) rank += __popc(w[q]);
+      row = base[e] + rank;
+      row_token[row] = t;
+    }
+    slot_row[s] = row;
+  }
+  if (x_perm == nullptr) return;
+
+  // rows: each wavefront copies its tokens' rows to their destinations with
+  // 16-byte vectors (destination rows recomputed from the bitmap)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nt = min(TB, Tn - t0);
   constexpr int EPC = 16 / sizeof(T);
@@ -114,22 +132,14 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const T* __restric
     const int t = t0 + tl;
     for (int j = 0; j < k; ++j) {
       const int e = ids[(int64_t)t * k + j];
-      int row = -1;
-      if (e >= 0 && e < E) {
-        const uint32_t* w = bits + e * WPB;
-        int rank = __popc(w[tl >> 5] & ((1u << (tl & 31)) - 1u));
-        for (int q = 0; q < (tl >> 5); ++q) rank += __popc(w[q]);
-        row = base[e] + rank;
-      }
-      if (lane == 0) {
-        slot_row[(int64_t)t * k + j] = row;
-        if (row >= 0) row_token[row] = t;
-      }
-      if (row >= 0) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)t * d);
-        u32x4* dst = reinterpret_cast<u32x4*>(x_perm + (int64_t)row * d);
-        for (int c = lane; c < nchunk; c += 64) dst[c] = src[c];
-      }
+      if (e < 0 || e >= E) continue;
+      const uint32_t* w = bits + e * WPB;
+      int rank = __popc(w[tl >> 5] & ((1u << (tl & 31)) - 1u));
+      for (int q = 0; q < (tl >> 5); ++q) rank += __popc(w[q]);
+      const int row = base[e] + rank;
+      const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)t * d);
+      u32x4* dst = reinterpret_cast<u32x4*>(x_perm + (int64_t)row * d);
+      for (int c = lane; c < nchunk; c += 64) dst[c] = src[c];
     }
   }
 }

@@ -127,6 +127,7 @@ hipError_t launch_router_gemm(int dtype, int64_t T, int64_t d, int64_t E, const 
                               const float* bias, float* logits, int num_cu, hipStream_t stream) {
   GemmArgs a{};
   a.A = x;
+  a.a_rows = nullptr;
   a.B0 = w_router;
   a.B1 = nullptr;
   a.b_stride = 0;
@@ -138,6 +139,7 @@ hipError_t launch_router_gemm(int dtype, int64_t T, int64_t d, int64_t E, const 
   a.C = logits;
   a.bias = bias;
   a.n_group = 0;
+  a.m_chunk = 0;
   const dim3 grid((unsigned)num_cu), block(512);
   if (dtype == 1)
     hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, 64, 4, 2, 2, EPI_F32_BIAS>), grid, block, 0, stream, a);

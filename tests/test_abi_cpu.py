@@ -56,9 +56,9 @@ def test_permute_workspace_query():
 
 
 def test_grouped_ffn_workspace_query():
-    st, n = q("moe_grouped_ffn", 5000, 256, 12, 192, 1, *([None] * 6))
+    st, n = q("moe_grouped_ffn", 5000, 256, 12, 192, 1, None, 0, *([None] * 6))
     assert st == OK and n == ru(5000 * 192 * 2)
-    st, n = q("moe_grouped_ffn", 5000, 256, 12, 192, 0, *([None] * 6))
+    st, n = q("moe_grouped_ffn", 5000, 256, 12, 192, 0, None, 0, *([None] * 6))
     assert st == OK and n == ru(5000 * 192 * 4)
 
 
@@ -117,9 +117,11 @@ def test_route_without_workspace_when_one_is_needed():
     assert st == WORKSPACE
 
 
-def ffn(n_max=1000, d=128, E=4, F=128, dt=1, xp=P, off=P, wg=P, wu=P, wd=P, yp=P, ws=P, nbytes=1 << 30):
+def ffn(n_max=1000, d=128, E=4, F=128, dt=1, xp=P, n_in=0, rows=None, off=P, wg=P, wu=P, wd=P, yp=P, ws=P,
+        nbytes=1 << 30):
     n = ctypes.c_size_t(nbytes)
-    return B.lib().moe_grouped_ffn(n_max, d, E, F, dt, xp, off, wg, wu, wd, yp, ws, ctypes.byref(n), None)
+    return B.lib().moe_grouped_ffn(n_max, d, E, F, dt, xp, n_in, rows, off, wg, wu, wd, yp, ws, ctypes.byref(n),
+                                   None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -127,6 +129,9 @@ def ffn(n_max=1000, d=128, E=4, F=128, dt=1, xp=P, off=P, wg=P, wu=P, wd=P, yp=P
     (dict(E=2000), UNSUPPORTED), (dict(n_max=1 << 31), UNSUPPORTED),
     (dict(xp=None), INVALID), (dict(off=None), INVALID), (dict(wg=None), INVALID), (dict(wu=P_MIS), INVALID),
     (dict(wd=None), INVALID), (dict(yp=P_MIS), INVALID), (dict(nbytes=1000 * 128 * 2 - 1), WORKSPACE),
+    # in-place gather: n_in rows of x, 32-bit byte offsets
+    (dict(rows=P, n_in=0), INVALID), (dict(rows=P, n_in=(1 << 31) // 128), UNSUPPORTED),
+    (dict(rows=ctypes.c_void_p(0x10001), n_in=100), INVALID),
 ])
 def test_grouped_ffn_argument_errors(kw, status):
     assert ffn(**kw) == status

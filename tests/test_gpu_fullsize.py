@@ -86,9 +86,8 @@ def test_full_size_sampled_parity(name):
         ids, w, _ = B.moe_route(inp["x"], inp["w_router"], wl.k, bias=inp["bias"], want_logits=False)
     else:
         ids, w = inp["topk_ids"], inp["topk_w"]
-    off, rt, sr, xp = B.moe_permute(inp["x"], ids, wl.E)
-    yp = B.moe_grouped_ffn(xp, off, inp["w_gate"], inp["w_up"], inp["w_down"])
-    del xp
+    off, rt, sr, _ = B.moe_permute(inp["x"], ids, wl.E, copy_rows=False)
+    yp = B.moe_grouped_ffn(inp["x"], off, inp["w_gate"], inp["w_up"], inp["w_down"], a_rows=rt)
     y = B.moe_combine(yp, sr, w)
     torch.cuda.synchronize()
     assert bits_equal(y, L.y)

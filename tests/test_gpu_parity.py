@@ -97,6 +97,11 @@ def test_permute_bit_exact(T, E, k, drop, dtype):
     assert np.array_equal(i64(sr), r_sr)
     idx = torch.from_numpy(r_rt.astype(np.int64)).to(DEV)
     assert bits_equal(xp[:N], x[idx])
+    # indices only (no row copy): the same indices
+    off2, rt2, sr2, none = B.moe_permute(x, torch.from_numpy(ids).to(DEV), E, copy_rows=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(off, off2) and torch.equal(rt[:N], rt2[:N]) and torch.equal(sr, sr2)
 
 
 # ---------------------------------------------------------------------------
@@ -124,6 +129,14 @@ def test_grouped_ffn_matches_oracle(counts, d, F, dtype):
     torch.cuda.synchronize()
     ref = orc.grouped_ffn(f64(xp[:N]), off, LazyExperts(wg), LazyExperts(wu), LazyExperts(wd))
     assert_close(f64(yp[:N]), ref, dtype, "y_perm")
+    # the same rows read in place from a token matrix through a gather map: bit-equal
+    T = 3 * N + 5
+    rows = torch.from_numpy(np.random.default_rng(17).choice(T, size=N, replace=N > T).astype(np.int32)).to(DEV)
+    x = torch.randn(T, d, generator=gen, device=DEV).to(dtype)
+    x[rows.long()] = xp[:N]
+    yg = B.moe_grouped_ffn(x, torch.from_numpy(off).to(DEV), wg, wu, wd, a_rows=rows, n_max=n_max)
+    torch.cuda.synchronize()
+    assert bits_equal(yg[:N], yp[:N])
 
 
 def test_grouped_ffn_in_place_over_x_perm():
@@ -188,8 +201,10 @@ def test_layer_forward_equals_stage_by_stage():
     off, rt, sr, xp = B.moe_permute(inp["x"], ids, wl.E)
     yp = B.moe_grouped_ffn(xp, off, inp["w_gate"], inp["w_up"], inp["w_down"])
     y = B.moe_combine(yp, sr, w)
+    yp2 = B.moe_grouped_ffn(inp["x"], off, inp["w_gate"], inp["w_up"], inp["w_down"], a_rows=rt)
+    y2 = B.moe_combine(yp2, sr, w)
     torch.cuda.synchronize()
-    assert bits_equal(L.y, y)
+    assert bits_equal(L.y, y) and bits_equal(L.y, y2)
 
 
 PRE_ROUTED = [W.Workload("pre_small", T=2000, d=256, E=24, k=8, F=192, dtype=torch.bfloat16, routing="pre_routed",
