@@ -38,7 +38,9 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
   *reinterpret_cast<f32x4*>(p + 4) = b;
 }
 
-template <typename T>
+// KU > 0: k is the compile-time KU, so the token's KU row loads are all in
+// flight before the first FMA; KU == 0: any k, in groups of 8.
+template <typename T, int KU>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_perm, const int32_t* __restrict__ slot_row,
                                                       const float* __restrict__ w, int Tn, int d, int k,
                                                       T* __restrict__ y) {
@@ -47,20 +49,60 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_pe
   const int lane = threadIdx.x & 63;
   const int32_t* sr = slot_row + (int64_t)t * k;
   const float* wt = w + (int64_t)t * k;
-  for (int c0 = lane * 8; c0 < d; c0 += 64 * 8) {
-    float acc[8];
+  if constexpr (KU > 0) {
+    int row[KU];
+    float wj[KU];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int row = sr[j];
-      if (row < 0) continue;
-      const float wj = wt[j];
-      float v[8];
-      load8(y_perm + (int64_t)row * d + c0, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+    for (int j = 0; j < KU; ++j) {
+      row[j] = __builtin_amdgcn_readfirstlane(sr[j]);
+      wj[j] = wt[j];
     }
-    store8(y + (int64_t)t * d + c0, acc);
+    for (int c0 = lane * 8; c0 < d; c0 += 64 * 8) {
+      float v[KU][8];
+#pragma unroll
+      for (int j = 0; j < KU; ++j)
+        if (row[j] >= 0) load8(y_perm + (int64_t)row[j] * d + c0, v[j]);
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < KU; ++j)
+        if (row[j] >= 0) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj[j], v[j][i], acc[i]);
+        }
+      store8(y + (int64_t)t * d + c0, acc);
+    }
+  } else {
+    for (int c0 = lane * 8; c0 < d; c0 += 64 * 8) {
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+      for (int j = 0; j < k; ++j) {
+        const int row = sr[j];
+        if (row < 0) continue;
+        const float wj = wt[j];
+        float v[8];
+        load8(y_perm + (int64_t)row * d + c0, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+      }
+      store8(y + (int64_t)t * d + c0, acc);
+    }
+  }
+}
+
+template <typename T>
+void launch_combine_t(int64_t T_, int64_t d, int64_t k, const T* y_perm, const int32_t* slot_row, const float* w,
+                      T* y, hipStream_t stream) {
+  const dim3 grid((unsigned)((T_ + 3) / 4)), block(256);
+  const int Tn = (int)T_, dn = (int)d, kn = (int)k;
+  switch (k) {
+    case 1: hipLaunchKernelGGL((combine_kernel<T, 1>), grid, block, 0, stream, y_perm, slot_row, w, Tn, dn, kn, y); break;
+    case 2: hipLaunchKernelGGL((combine_kernel<T, 2>), grid, block, 0, stream, y_perm, slot_row, w, Tn, dn, kn, y); break;
+    case 4: hipLaunchKernelGGL((combine_kernel<T, 4>), grid, block, 0, stream, y_perm, slot_row, w, Tn, dn, kn, y); break;
+    case 8: hipLaunchKernelGGL((combine_kernel<T, 8>), grid, block, 0, stream, y_perm, slot_row, w, Tn, dn, kn, y); break;
+    default: hipLaunchKernelGGL((combine_kernel<T, 0>), grid, block, 0, stream, y_perm, slot_row, w, Tn, dn, kn, y);
   }
 }
 
@@ -68,13 +110,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_pe
 
 hipError_t launch_combine(int dtype, int64_t T, int64_t d, int64_t k, const void* y_perm, const int32_t* slot_row,
                           const float* w, void* y, hipStream_t stream) {
-  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
   if (dtype == 1)
-    hipLaunchKernelGGL(combine_kernel<bf16>, grid, block, 0, stream, (const bf16*)y_perm, slot_row, w, (int)T, (int)d,
-                       (int)k, (bf16*)y);
+    launch_combine_t<bf16>(T, d, k, (const bf16*)y_perm, slot_row, w, (bf16*)y, stream);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, stream, (const float*)y_perm, slot_row, w, (int)T,
-                       (int)d, (int)k, (float*)y);
+    launch_combine_t<float>(T, d, k, (const float*)y_perm, slot_row, w, (float*)y, stream);
   return hipGetLastError();
 }
 
