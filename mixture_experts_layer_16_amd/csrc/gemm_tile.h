@@ -27,6 +27,12 @@ enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2 };
 
 constexpr int kMaxGroups = 1024;
 constexpr int kXcds = 8;   // accelerator complex dies of an MI355X, one L2 each
+// Issue the next tile's first copies before this tile's epilogue (they overlap the
+// stores) rather than after it.
+#ifndef MOE_COPIES_OVER_EPILOGUE
+#define MOE_COPIES_OVER_EPILOGUE 1
+#endif
+constexpr bool kCopiesOverEpilogue = MOE_COPIES_OVER_EPILOGUE;
 
 struct GemmArgs {
   const void* A;          // [rows, K]; group g owns rows seg[g] .. seg[g+1]-1
@@ -223,18 +229,21 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   const T* __restrict__ Abase = static_cast<const T*>(p.A);
 
   // ---- tile bookkeeping (all wave-uniform) ------------------------------------
-  int g = 0, n0 = 0, rows_valid = 0;
-  int64_t m0 = 0;
-  auto locate = [&](int tile) {
+  struct TileInfo {
+    int g, n0, rows_valid;
+    int64_t m0;
+  };
+  auto locate = [&](int tile) -> TileInfo {
     int lo = 0, hi = G;                      // largest g with tstart[g] <= tile
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (tstart[mid] <= tile) lo = mid; else hi = mid;
     }
-    g = __builtin_amdgcn_readfirstlane(lo);
-    const int local = tile - __builtin_amdgcn_readfirstlane(tstart[g]);
-    const int64_t seg_lo = p.seg ? (int64_t)p.seg[g] : 0;
-    const int64_t seg_hi = p.seg ? (int64_t)p.seg[g + 1] : p.M;
+    TileInfo t;
+    t.g = __builtin_amdgcn_readfirstlane(lo);
+    const int local = tile - __builtin_amdgcn_readfirstlane(tstart[t.g]);
+    const int64_t seg_lo = p.seg ? (int64_t)p.seg[t.g] : 0;
+    const int64_t seg_hi = p.seg ? (int64_t)p.seg[t.g + 1] : p.M;
     // Within a group the tiles run in chunks of SM row tiles; inside a chunk, in
     // column groups of NG column tiles; inside a column group, row tile by row
     // tile.  Consecutive tiles then share A rows (same row tile) and B columns
@@ -251,9 +260,23 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     const int l2 = l - cg * sm * NG;
     const int sz = min(NG, ntn - cg * NG);
     const int mt = base_m + l2 / sz, nt = cg * NG + l2 % sz;
-    m0 = seg_lo + (int64_t)mt * BM;
-    n0 = nt * NOUT;
-    rows_valid = (int)min<int64_t>(BM, seg_hi - m0);
+    t.m0 = seg_lo + (int64_t)mt * BM;
+    t.n0 = nt * NOUT;
+    t.rows_valid = (int)min<int64_t>(BM, seg_hi - t.m0);
+    return t;
+  };
+
+  // A rows this lane copies for a tile: load step i (< CPA) covers LDS rows
+  // [i*kRowsPerStep, (i+1)*kRowsPerStep) of the A region.  With a gather map the
+  // row numbers are fetched from it (early, so the fetch hides under a K loop).
+  constexpr int CPA = BM / Cfg::kRowsPerStep;
+  auto fetch_rows = [&](const TileInfo& t, int* arow) {
+#pragma unroll
+    for (int i = 0; i < CPA; ++i) {
+      const int row = (i * NT + tid) * 16 / RB;
+      const int r = min(row, t.rows_valid - 1);              // rows past the segment: any valid row
+      arow[i] = p.a_rows ? p.a_rows[t.m0 + r] : r;
+    }
   };
 
   // Uniform (SGPR) tile bases plus a fixed 32-bit byte offset per lane and load
@@ -262,27 +285,26 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   const char* Bgb = nullptr;
   const char* Bub = nullptr;
   uint32_t soff[CPT];
-  auto setup = [&]() {
-    Ab = reinterpret_cast<const char*>(p.a_rows ? Abase : Abase + m0 * K);
-    Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)g * p.b_stride + (int64_t)n0 * K);
+  auto setup = [&](const TileInfo& t, const int* arow) {
+    Ab = reinterpret_cast<const char*>(p.a_rows ? Abase : Abase + t.m0 * K);
+    Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)t.g * p.b_stride + (int64_t)t.n0 * K);
     if (EPI == EPI_SWIGLU)
-      Bub = reinterpret_cast<const char*>(static_cast<const T*>(p.B1) + (int64_t)g * p.b_stride + (int64_t)n0 * K);
+      Bub = reinterpret_cast<const char*>(static_cast<const T*>(p.B1) + (int64_t)t.g * p.b_stride +
+                                          (int64_t)t.n0 * K);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      // load step i covers LDS rows [i*kRowsPerStep, (i+1)*kRowsPerStep); whether
-      // it reads A, gate or up is known at compile time
+      // whether load step i reads A, gate or up is known at compile time
       const int byte = (i * NT + tid) * 16;
       const int row = byte / RB;
       const int lc = Cfg::swz(row, (byte % RB) / 16);
       int r;
-      if (row < BM) {
-        r = min(row, rows_valid - 1);                         // rows past the segment: any valid row
-        if (p.a_rows) r = p.a_rows[m0 + r];                   // gathered row of A
+      if (i < CPA) {
+        r = arow[i];
       } else {
         const int br = row - BM;
         const int half = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
         const int n = (br < half) ? br : br - half;
-        r = min(n, p.N - n0 - 1);                              // columns past N: any valid column
+        r = min(n, p.N - t.n0 - 1);                            // columns past N: any valid column
       }
       soff[i] = ((uint32_t)r * (uint32_t)K + (uint32_t)(lc * EPC)) * (uint32_t)sizeof(T);
     }
@@ -356,8 +378,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   const int step = grid, end = total;
   if (grid % kXcds == 0) tile = (blockIdx.x % kXcds) * (grid / kXcds) + blockIdx.x / kXcds;
   if (tile >= end) return;
-  locate(tile);
-  setup();
+  TileInfo cur = locate(tile), nxt = cur;
+  int arow[CPA], arow_n[CPA];
+  fetch_rows(cur, arow);
+  setup(cur, arow);
   prologue();
 
   while (true) {
@@ -368,13 +392,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
 
-    mi_live = __builtin_amdgcn_readfirstlane(min(MI, max(0, (rows_valid - wm * Cfg::WTM + 31) / 32)));
+    mi_live = __builtin_amdgcn_readfirstlane(min(MI, max(0, (cur.rows_valid - wm * Cfg::WTM + 31) / 32)));
 
     // k-tile 0 has landed (this wave's copies; the barrier covers the others)
     if (STAGES - 2 <= nk - 1) wait_vmcnt<(STAGES - 2) * CPT>();
     else wait_vmcnt<0>();
     block_barrier();
     if (STAGES - 1 < nk) load_stage((STAGES - 1) % STAGES, STAGES - 1);
+    // look up the next tile now; its row numbers arrive during this K loop
+    const int next_tile = tile + step;
+    const bool more = next_tile < end;
+    if (more) {
+      nxt = locate(next_tile);
+      fetch_rows(nxt, arow_n);
+    }
 #pragma unroll
     for (int s = 0; s < PD; ++s) read_frags(s, 0, s);
 
@@ -401,18 +432,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     }
 
     // this tile's LDS reads are done everywhere: start the next tile's copies, then
-    // store this tile from registers while they are in flight
+    // store this tile while they are in flight
     wait_lgkmcnt0();
     block_barrier();
-    const int64_t em0 = m0;
-    const int en0 = n0, erows = rows_valid;
-    tile += step;
-    const bool more = tile < end;
-    if (more) {
-      locate(tile);
-      setup();
-      prologue();
+    if constexpr (kCopiesOverEpilogue) {
+      if (more) {
+        setup(nxt, arow_n);
+        prologue();
+      }
     }
+    const int64_t em0 = cur.m0;
+    const int en0 = cur.n0, erows = cur.rows_valid;
 
     // ---- epilogue.  Block (mi, ni): lane holds output row (lane % 32) and the
     //      columns 8*q + 4*(lane/32) + i in acc[4*q + i], q, i = 0..3 -----------
@@ -441,6 +471,64 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
                 if (col + i < p.N) crow[col + i] = acc[mi][ni][4 * q + i] + (p.bias ? p.bias[col + i] : 0.f);
             }
           }
+      }
+    } else if constexpr (NT == 512 && Cfg::WTM == 64 && 8 * 32 * 144 <= Cfg::kStageBytes) {
+      // Staged through LDS, in the last pipeline stage (the next tile writes it only
+      // after its first barrier).  Each wave owns 32 rows x 144 bytes: per round
+      // (one row block mi, 128 bytes of output columns) it parks its values there
+      // (the 16-byte pad spreads rows over the banks and keeps every address a lane
+      // base plus an immediate), then reads them back as 16-byte pieces, 8 lanes per
+      // row, and stores whole 128-byte row segments.
+      constexpr int NO = (EPI == EPI_SWIGLU) ? NI / 2 : NI;
+      constexpr int CW = (EPI == EPI_SWIGLU) ? Cfg::WTN / 2 : Cfg::WTN;   // output columns per wave
+      constexpr int ES = (int)sizeof(T);
+      constexpr int RC = 128 / ES;                                         // columns per round
+      constexpr int ROUNDS = CW / RC;
+      constexpr int RS = 144;                                              // staging row stride (bytes)
+      static_assert(CW % RC == 0, "whole rounds");
+      char* wbuf = smem + (STAGES - 1) * Cfg::kStageBytes + wave * (32 * RS);
+      char* wlane = wbuf + (lane & 31) * RS + h4 * ES;                     // this lane's row and column offset
+      const char* rlane = wbuf + (lane >> 3) * RS + (lane & 7) * 16;
+      // read-back rows r0 + 32 mi + 8 it of this wave; one 64-bit address per lane,
+      // stepped by scalars (no per-row 64-bit products to keep live)
+      const int r0 = wm * Cfg::WTM + (lane >> 3);
+      const int rrem = erows - r0;
+      const int c0l = en0 + wn * CW + (lane & 7) * (16 / ES);
+      T* cbase = static_cast<T*>(p.C) + (em0 + r0) * (int64_t)p.N + c0l;
+      const int64_t rstep = 8 * (int64_t)p.N;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        if (mi >= mi_live) break;
+#pragma unroll
+        for (int rd = 0; rd < ROUNDS; ++rd) {
+#pragma unroll
+          for (int ni = 0; ni < NO; ++ni)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int c0 = ni * 32 + 8 * q - rd * RC;                  // compile time
+              if (c0 < 0 || c0 >= RC) continue;
+              float v[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                if constexpr (EPI == EPI_SWIGLU) {
+                  const float gv = acc[mi][ni][4 * q + i];
+                  const float uv = acc[mi][ni + NI / 2][4 * q + i];
+                  v[i] = gv / (1.0f + __expf(-gv)) * uv;
+                } else {
+                  v[i] = acc[mi][ni][4 * q + i];
+                }
+              }
+              store4(reinterpret_cast<T*>(wlane + c0 * ES), v);
+            }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+          for (int it = 0; it < 4; ++it) {
+            const u32x4 val = *reinterpret_cast<const u32x4*>(rlane + it * 8 * RS);
+            if (mi * 32 + it * 8 < rrem && c0l + rd * RC < p.N)
+              *reinterpret_cast<u32x4*>(cbase + (4 * mi + it) * rstep + rd * RC) = val;
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
       }
     } else {
       constexpr int NO = (EPI == EPI_SWIGLU) ? NI / 2 : NI;
@@ -473,6 +561,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
       }
     }
     if (!more) break;
+    if constexpr (!kCopiesOverEpilogue) {
+      setup(nxt, arow_n);
+      prologue();
+    }
+    tile = next_tile;
+    cur = nxt;
   }
 }
 
