@@ -19,20 +19,32 @@
 //    round trip; an empty group owns no tile and its weights are never read.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
 
 enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2 };
 
+// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
+template <int N, int I = 0, typename F> __device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 constexpr int kMaxGroups = 1024;
 constexpr int kXcds = 8;   // accelerator complex dies of an MI355X, one L2 each
-// Issue the next tile's first copies before this tile's epilogue (they overlap the
-// stores) rather than after it.
-#ifndef MOE_COPIES_OVER_EPILOGUE
-#define MOE_COPIES_OVER_EPILOGUE 1
+// A recycled stage's copies are threaded between the MFMAs of the kDmaSpread
+// sub-steps that follow the barrier (0: all issued at the barrier).  Issued as one
+// burst, the copies of eight waves queue up in the vector-memory path and hold up
+// the MFMAs behind them in every wave.
+#ifndef MOE_DMA_SPREAD
+#define MOE_DMA_SPREAD 1
 #endif
-constexpr bool kCopiesOverEpilogue = MOE_COPIES_OVER_EPILOGUE;
+constexpr int kDmaSpread = MOE_DMA_SPREAD;
 
 struct GemmArgs {
   const void* A;          // [rows, K]; group g owns rows seg[g] .. seg[g+1]-1
@@ -104,7 +116,15 @@ __device__ __forceinline__ void lds_dma16(const char* gbase, uint32_t voff, uint
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Wait for every outstanding LDS (and scalar-memory) access of this wave.  Issued
+// through the builtin, which the compiler's own wait insertion accounts for (an
+// inline-asm wait is opaque to it, and it would then wait again later for reads
+// that have already landed); the empty asm keeps memory accesses from moving
+// across.  Encoding (gfx9): vmcnt 63, expcnt 7, lgkmcnt 0.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+}
 // Workgroup barrier without the memory fence of __syncthreads (which would
 // also drain every outstanding prefetch).
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -198,7 +218,7 @@ __device__ void build_tile_prefix(const int32_t* seg, int G, int64_t M, int ntn,
   __syncthreads();
 }
 
-// PD: how many 16-k sub-steps ahead the MFMA operand fragments are read from LDS.
+// PD: how many 16-k sub-steps ahead the MFMA operand fragments are read from LDS
 template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, int PD = 1>
 __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs p) {
   typedef GemmTile<T, BM, BN, BK, WM, WN, STAGES, EPI> Cfg;
@@ -212,6 +232,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   constexpr int KSUB = Cfg::kSub;
   static_assert(PD >= 1 && PD < KSUB, "prefetch distance must be 1 .. sub-steps - 1");
 
+  constexpr int kEpiRowBytes = 144;                 // staging row stride of the epilogue (bytes)
+  constexpr int kEpiWaveBytes = 32 * kEpiRowBytes;  // one wave's staging buffer: 32 rows
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::kLdsBytes];
   __shared__ int tstart[kMaxGroups + 1];
 
@@ -309,18 +331,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
       soff[i] = ((uint32_t)r * (uint32_t)K + (uint32_t)(lc * EPC)) * (uint32_t)sizeof(T);
     }
   };
-  auto load_stage = [&](int stage, int kt) {
+  // copy i (of CPT) of k-tile kt into `stage`
+  auto load_one = [&](int stage, int kt, int i) {
     const uint32_t lbase = lds_addr_of(smem) + stage * Cfg::kStageBytes + wave * 64 * 16;
     const int64_t kb = (int64_t)kt * BK * (int64_t)sizeof(T);
+    const int row0 = i * Cfg::kRowsPerStep;
+    const char* base;
+    if (row0 < BM) base = Ab;
+    else if (EPI == EPI_SWIGLU && row0 - BM >= BN / 2) base = Bub;
+    else base = Bgb;
+    lds_dma16(base + kb, soff[i], lbase + i * NT * 16);
+  };
+  auto load_stage = [&](int stage, int kt) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int row0 = i * Cfg::kRowsPerStep;
-      const char* base;
-      if (row0 < BM) base = Ab;
-      else if (EPI == EPI_SWIGLU && row0 - BM >= BN / 2) base = Bub;
-      else base = Bgb;
-      lds_dma16(base + kb, soff[i], lbase + i * NT * 16);
-    }
+    for (int i = 0; i < CPT; ++i) load_one(stage, kt, i);
   };
   auto prologue = [&]() {
 #pragma unroll
@@ -335,13 +359,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   // ---- MFMA operand fragments: one buffer per sub-step of a k-tile, read PD
   //      sub-steps ahead of the MFMAs that use them -------------------------------
   typename Op::Frag fa[KSUB][MI], fb[KSUB][NI];
-  auto read_frags = [&](int buf, int stage, int sub) {
+  // full: every row block of this wave is live (no per-block checks)
+  auto read_frags = [&](bool full, int buf, int stage, int sub) {
     const char* sA = smem + stage * Cfg::kStageBytes;
     const char* sB = sA + BM * RB;
     const int lc0 = sub * 2 * Cfg::CPL + (lane >> 5) * Cfg::CPL;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      if (mi >= mi_live) continue;
+      if (!full && mi >= mi_live) continue;
       const int r = wm * Cfg::WTM + mi * 32 + (lane & 31);
       if constexpr (Op::kReads == 1)
         Op::load(fa[buf][mi], sA + r * RB + Cfg::swz(r, lc0) * 16);
@@ -360,92 +385,40 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   f32x16 acc[MI][NI];
   // B (weights) is the MFMA's first operand: each block comes out transposed, so a
   // lane ends up holding 4 consecutive output columns of one row.
-  auto mma_all = [&](int buf) {
+  auto mma_all = [&](bool full, int buf) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
-      if (mi < mi_live) {
+      if (full || mi < mi_live) {
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) Op::mma(fb[buf][ni], fa[buf][mi], acc[mi][ni]);
       }
   };
-
-  // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b on XCD b % 8)
-  // and each XCD has its own L2.  Give the workgroups of one XCD a contiguous run
-  // of the tile list in every round, so that the tiles resident on an XCD share
-  // their A rows (the column tiles of a row tile) and expert weights.
-  const int grid = gridDim.x;
-  int tile = blockIdx.x;
-  const int step = grid, end = total;
-  if (grid % kXcds == 0) tile = (blockIdx.x % kXcds) * (grid / kXcds) + blockIdx.x / kXcds;
-  if (tile >= end) return;
-  TileInfo cur = locate(tile), nxt = cur;
-  int arow[CPA], arow_n[CPA];
-  fetch_rows(cur, arow);
-  setup(cur, arow);
-  prologue();
-
-  while (true) {
+  // the same MFMAs with copies J0 .. J1-1 of k-tile kt into `stage` (if copy)
+  // threaded between them
+  auto mma_all_copy = [&](auto j0c, auto j1c, bool full, int buf, int stage, int kt, bool copy) {
+    constexpr int J0 = decltype(j0c)::value, J1 = decltype(j1c)::value;
+    constexpr int NM = MI * NI, NJ = J1 - J0;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
+      for (int ni = 0; ni < NI; ++ni) {
+        if (full || mi < mi_live) Op::mma(fb[buf][ni], fa[buf][mi], acc[mi][ni]);
+        const int q = mi * NI + ni;
+        // copies go after MFMAs q with q * NJ / NM stepping up
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
-
-    mi_live = __builtin_amdgcn_readfirstlane(min(MI, max(0, (cur.rows_valid - wm * Cfg::WTM + 31) / 32)));
-
-    // k-tile 0 has landed (this wave's copies; the barrier covers the others)
-    if (STAGES - 2 <= nk - 1) wait_vmcnt<(STAGES - 2) * CPT>();
-    else wait_vmcnt<0>();
-    block_barrier();
-    if (STAGES - 1 < nk) load_stage((STAGES - 1) % STAGES, STAGES - 1);
-    // look up the next tile now; its row numbers arrive during this K loop
-    const int next_tile = tile + step;
-    const bool more = next_tile < end;
-    if (more) {
-      nxt = locate(next_tile);
-      fetch_rows(nxt, arow_n);
-    }
-#pragma unroll
-    for (int s = 0; s < PD; ++s) read_frags(s, 0, s);
-
-    for (int kt = 0; kt < nk; ++kt) {
-      const int st = kt % STAGES;
-#pragma unroll
-      for (int s = 0; s < KSUB; ++s) {
-        if (s + PD < KSUB) {
-          read_frags(s + PD, st, s + PD);
-        } else if (kt + 1 < nk) {
-          if (s + PD == KSUB) {
-            // every LDS read of stage st has been issued: wait for them, and for
-            // k-tile kt+1 to land, then recycle stage st for k-tile kt+STAGES
-            wait_lgkmcnt0();
-            if (kt + STAGES - 1 <= nk - 1) wait_vmcnt<(STAGES - 2) * CPT>();
-            else wait_vmcnt<0>();
-            block_barrier();
-            if (kt + STAGES < nk) load_stage(st, kt + STAGES);
-          }
-          read_frags(s + PD - KSUB, (kt + 1) % STAGES, s + PD - KSUB);
-        }
-        mma_all(s);
+        for (int j = J0 + q * NJ / NM; j < J0 + (q + 1) * NJ / NM; ++j)
+          if (copy) load_one(stage, kt, j);
       }
-    }
+  };
 
-    // this tile's LDS reads are done everywhere: start the next tile's copies, then
-    // store this tile while they are in flight
-    wait_lgkmcnt0();
-    block_barrier();
-    if constexpr (kCopiesOverEpilogue) {
-      if (more) {
-        setup(nxt, arow_n);
-        prologue();
-      }
-    }
-    const int64_t em0 = cur.m0;
-    const int en0 = cur.n0, erows = cur.rows_valid;
+  // ---- epilogue: store the accumulators of tile t (this wave's part).  Block
+  //      (mi, ni): lane holds output row (lane % 32) and the columns
+  //      8*q + 4*(lane/32) + i in acc[4*q + i], q, i = 0..3.  wbuf: this wave's
+  //      LDS staging buffer (kEpiWaveBytes). -----------------------------------
+  auto store_tile = [&](const TileInfo& t, char* wbuf) {
+    const int64_t em0 = t.m0;
+    const int en0 = t.n0, erows = t.rows_valid;
 
-    // ---- epilogue.  Block (mi, ni): lane holds output row (lane % 32) and the
-    //      columns 8*q + 4*(lane/32) + i in acc[4*q + i], q, i = 0..3 -----------
     const int h4 = 4 * (lane >> 5);
     if constexpr (EPI == EPI_F32_BIAS) {
 #pragma unroll
@@ -472,9 +445,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
             }
           }
       }
-    } else if constexpr (NT == 512 && Cfg::WTM == 64 && 8 * 32 * 144 <= Cfg::kStageBytes) {
-      // Staged through LDS, in the last pipeline stage (the next tile writes it only
-      // after its first barrier).  Each wave owns 32 rows x 144 bytes: per round
+    } else if constexpr (NT == 512 && Cfg::WTM == 64 && 8 * kEpiWaveBytes <= Cfg::kStageBytes) {
+      // Staged through LDS (wbuf: this wave's 32 rows x 144 bytes, which nothing
+      // else touches until the next barrier).  Per round
       // (one row block mi, 128 bytes of output columns) it parks its values there
       // (the 16-byte pad spreads rows over the banks and keeps every address a lane
       // base plus an immediate), then reads them back as 16-byte pieces, 8 lanes per
@@ -484,9 +457,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
       constexpr int ES = (int)sizeof(T);
       constexpr int RC = 128 / ES;                                         // columns per round
       constexpr int ROUNDS = CW / RC;
-      constexpr int RS = 144;                                              // staging row stride (bytes)
+      constexpr int RS = kEpiRowBytes;
       static_assert(CW % RC == 0, "whole rounds");
-      char* wbuf = smem + (STAGES - 1) * Cfg::kStageBytes + wave * (32 * RS);
       char* wlane = wbuf + (lane & 31) * RS + h4 * ES;                     // this lane's row and column offset
       const char* rlane = wbuf + (lane >> 3) * RS + (lane & 7) * 16;
       // read-back rows r0 + 32 mi + 8 it of this wave; one 64-bit address per lane,
@@ -520,14 +492,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
               }
               store4(reinterpret_cast<T*>(wlane + c0 * ES), v);
             }
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          wait_lgkmcnt0();
 #pragma unroll
           for (int it = 0; it < 4; ++it) {
             const u32x4 val = *reinterpret_cast<const u32x4*>(rlane + it * 8 * RS);
             if (mi * 32 + it * 8 < rrem && c0l + rd * RC < p.N)
               *reinterpret_cast<u32x4*>(cbase + (4 * mi + it) * rstep + rd * RC) = val;
           }
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          wait_lgkmcnt0();
         }
       }
     } else {
@@ -560,11 +532,106 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
           }
       }
     }
-    if (!more) break;
-    if constexpr (!kCopiesOverEpilogue) {
+  };
+
+  // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b on XCD b % 8)
+  // and each XCD has its own L2.  Give the workgroups of one XCD a contiguous run
+  // of the tile list in every round, so that the tiles resident on an XCD share
+  // their A rows (the column tiles of a row tile) and expert weights.
+  const int grid = gridDim.x;
+  int tile = blockIdx.x;
+  const int step = grid, end = total;
+  if (grid % kXcds == 0) tile = (blockIdx.x % kXcds) * (grid / kXcds) + blockIdx.x / kXcds;
+  if (tile >= end) return;
+
+  TileInfo cur = locate(tile), nxt = cur;
+  int arow[CPA], arow_n[CPA];
+  fetch_rows(cur, arow);
+  setup(cur, arow);
+  prologue();
+
+  while (true) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
+
+    mi_live = __builtin_amdgcn_readfirstlane(min(MI, max(0, (cur.rows_valid - wm * Cfg::WTM + 31) / 32)));
+
+    // k-tile 0 has landed (this wave's copies; the barrier covers the others)
+    if (STAGES - 2 <= nk - 1) wait_vmcnt<(STAGES - 2) * CPT>();
+    else wait_vmcnt<0>();
+    block_barrier();
+    if (STAGES - 1 < nk) load_stage((STAGES - 1) % STAGES, STAGES - 1);
+    // look up the next tile now; its row numbers arrive during this K loop
+    const int next_tile = tile + step;
+    const bool more = next_tile < end;
+    if (more) {
+      nxt = locate(next_tile);
+      fetch_rows(nxt, arow_n);
+    }
+      // the K loop, compiled twice: without per-block checks for tiles whose row
+    // blocks are all live, with them for ragged tiles (the checks cost the
+    // compiler its exact tracking of outstanding LDS reads)
+    auto kloop = [&](auto fullc) {
+      constexpr bool FULL = decltype(fullc)::value;
+#pragma unroll
+      for (int s = 0; s < PD; ++s) read_frags(FULL, s, 0, s);
+
+      for (int kt = 0; kt < nk; ++kt) {
+        const int st = kt % STAGES;
+        static_for<KSUB>([&](auto sc) {
+          constexpr int s = decltype(sc)::value;
+          if constexpr (s + PD < KSUB) {
+            read_frags(FULL, s + PD, st, s + PD);
+          } else {
+            // every LDS read of stage st has been issued: wait for them (on every
+            // path, so the compiler sees one state after the branch)
+            if constexpr (s + PD == KSUB) wait_lgkmcnt0();
+            if (kt + 1 < nk) {
+              if constexpr (s + PD == KSUB) {
+                // k-tile kt+1 has landed: recycle stage st for k-tile kt+STAGES
+                if (kt + STAGES - 1 <= nk - 1) wait_vmcnt<(STAGES - 2) * CPT>();
+                else wait_vmcnt<0>();
+                block_barrier();
+                if (kDmaSpread == 0 && kt + STAGES < nk) load_stage(st, kt + STAGES);
+              }
+              read_frags(FULL, s + PD - KSUB, (kt + 1) % STAGES, s + PD - KSUB);
+            }
+          }
+          // copies threaded through sub-step KSUB-PD (this k-tile) and sub-steps
+          // 0 .. kDmaSpread-2 of the next one: piece i of kDmaSpread
+          constexpr int piece = (s + PD == KSUB) ? 0 : (s + 1 < kDmaSpread ? s + 1 : -1);
+          if constexpr (kDmaSpread > 0 && piece >= 0) {
+            constexpr int J0 = piece * CPT / (kDmaSpread > 0 ? kDmaSpread : 1);
+            constexpr int J1 = (piece + 1) * CPT / (kDmaSpread > 0 ? kDmaSpread : 1);
+            if constexpr (piece == 0)
+              mma_all_copy(std::integral_constant<int, J0>{}, std::integral_constant<int, J1>{}, FULL, s, st,
+                           kt + STAGES, kt + 1 < nk && kt + STAGES < nk);
+            else   // the copies of the stage recycled at the previous k-tile's barrier
+              mma_all_copy(std::integral_constant<int, J0>{}, std::integral_constant<int, J1>{}, FULL, s,
+                           (kt + STAGES - 1) % STAGES, kt - 1 + STAGES, kt >= 1 && kt - 1 + STAGES < nk);
+          } else {
+            mma_all(FULL, s);
+          }
+        });
+      }
+    };
+    if (mi_live == MI) kloop(std::true_type{});
+    else kloop(std::false_type{});
+
+    // this tile's LDS reads are done everywhere: start the next tile's copies, then
+    // store this tile while they are in flight
+    wait_lgkmcnt0();
+    block_barrier();
+    if (more) {
       setup(nxt, arow_n);
       prologue();
     }
+    store_tile(cur, smem + (STAGES - 1) * Cfg::kStageBytes + wave * kEpiWaveBytes);
+    if (!more) break;
     tile = next_tile;
     cur = nxt;
   }
