@@ -1,6 +1,7 @@
-"""CPU oracle of the routed-MoE layer forward (float64, numpy).
+"""CPU oracles (float64, numpy): the routed-MoE layer forward, and Muon's
+Newton-Schulz orthogonalisation of whole matrices.
 
 Test infrastructure: only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import it.  The product path never does.
 """
-from . import moe_oracle  # noqa: F401
+from . import moe_oracle, muon_oracle  # noqa: F401
