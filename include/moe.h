@@ -159,6 +159,33 @@ moe_status moe_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
                              void* y, float* logits_out, int32_t* topk_ids, float* topk_w,
                              int32_t* offsets_out, void* ws, size_t* ws_bytes, void* stream);
 
+/*
+ * moe_newton_schulz: Muon's orthogonalisation of a batch of whole matrices
+ * ("Training a 1T-Parameter MoE on EU public infrastructure with PyTorch and
+ * TorchTitan", section "FlexShard: communication-free Muon": a few
+ * Newton-Schulz iterations over each whole matrix, experts kept whole on one
+ * rank).  For each of the n matrices G [R,C], working on its wide orientation
+ * (a tall G is transposed first and the result transposed back):
+ *     X = G / (||G||_F + eps);  `steps` times: A = X X^T, B = b A + c A A, X = a X + B X
+ * Muon's published quintic uses (a, b, c) = (3.4445, -4.7750, 2.0315), 5 steps,
+ * eps = 1e-7.  bf16 storage of X, A and B between the products, fp32
+ * accumulation and fp32 Frobenius norm (summed in a fixed order: results are
+ * bit-reproducible).
+ *   n                  matrices (<= 65536)
+ *   R, C               rows and columns of each, multiples of 64
+ *   dtype              MOE_BF16 only (MOE_F32: MOE_ERR_UNSUPPORTED)
+ *   steps              >= 0 (0: the normalised input)
+ *   g   [n,R,C] bf16   input, row-major, matrices back to back
+ *   x   [n,R,C] bf16   out, same layout; must not overlap g or ws
+ *   ws: query with ws == NULL; about 3 n R C + 2 n min(R,C)^2 bf16 elements.
+ * Errors: n, R, C <= 0, steps < 0 or eps < 0 or NaN: MOE_ERR_INVALID_ARG;
+ * R or C not a multiple of 64, dtype not bf16, sizes past the limits:
+ * MOE_ERR_UNSUPPORTED; g, x, ws not 16-byte aligned: MOE_ERR_INVALID_ARG.
+ */
+moe_status moe_newton_schulz(int64_t n, int64_t R, int64_t C, moe_dtype dtype, int64_t steps,
+                             float a, float b, float c, float eps, const void* g, void* x,
+                             void* ws, size_t* ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
-EXPORTS = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward")
+EXPORTS = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_newton_schulz")
 
 
 class MoEError(RuntimeError):
@@ -31,6 +31,7 @@ class MoEError(RuntimeError):
 _lib: Optional[ctypes.CDLL] = None
 
 _i64, _int, _vp, _szp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
+_f32 = ctypes.c_float
 _SIGS = {
     "moe_route": [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp],
     "moe_permute": [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp],
@@ -38,7 +39,10 @@ _SIGS = {
     "moe_combine": [_i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp],
     "moe_layer_forward": [_i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                           _vp, _vp, _szp, _vp],
+    "moe_newton_schulz": [_i64, _i64, _i64, _int, _i64, _f32, _f32, _f32, _f32, _vp, _vp, _vp, _szp, _vp],
 }
+
+MUON_COEFFS = (3.4445, -4.7750, 2.0315)
 
 
 def lib() -> ctypes.CDLL:
@@ -155,6 +159,32 @@ def moe_combine(y_perm, slot_row, topk_w, out=None):
     _check("moe_combine", lib().moe_combine(T, d, k, dtype_code(y_perm.dtype), _p(y_perm), _p(slot_row),
                                             _p(topk_w), _p(y), _stream(y_perm.device)))
     return y
+
+
+class NewtonSchulz:
+    """moe_newton_schulz on a fixed batch [n, R, C] (bf16) with its output and
+    workspace allocated once."""
+
+    def __init__(self, g, steps: int = 5, coeffs=MUON_COEFFS, eps: float = 1e-7):
+        if g.dim() == 2:
+            g = g.unsqueeze(0)
+        self.g, self.steps, self.coeffs, self.eps = g, steps, coeffs, eps
+        n, R, C = g.shape
+        self.args = (n, R, C, dtype_code(g.dtype), steps, *coeffs, eps)
+        self.x = torch.empty_like(g)
+        self.ws = _ws(_query("moe_newton_schulz", *self.args, _p(g), _p(self.x)), g.device)
+
+    def __call__(self):
+        n = ctypes.c_size_t(self.ws.numel())
+        _check("moe_newton_schulz", lib().moe_newton_schulz(*self.args, _p(self.g), _p(self.x), _p(self.ws),
+                                                            ctypes.byref(n), _stream(self.g.device)))
+        return self.x
+
+
+def moe_newton_schulz(g, steps: int = 5, coeffs=MUON_COEFFS, eps: float = 1e-7):
+    """Muon's Newton-Schulz orthogonalisation of g [R, C] or [n, R, C] (bf16)."""
+    out = NewtonSchulz(g, steps, coeffs, eps)()
+    return out if g.dim() == 3 else out[0]
 
 
 class LayerForward:

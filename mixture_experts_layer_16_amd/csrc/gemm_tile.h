@@ -25,7 +25,7 @@
 
 namespace moe {
 
-enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2 };
+enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2, EPI_AXPBY = 3 };
 
 // f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
 template <int N, int I = 0, typename F> __device__ __forceinline__ void static_for(F&& f) {
@@ -53,15 +53,19 @@ struct GemmArgs {
   const void* B0;         // group g: B0 + g * b_stride elements, [N, K]
   const void* B1;         // EPI_SWIGLU: the "up" matrix, same layout as B0
   int64_t b_stride;       // elements between two groups' B matrices
-  const int32_t* seg;     // [G+1] device row offsets; nullptr = one group, rows [0, M)
+  const int32_t* seg;     // [G+1] device row offsets; nullptr: see group_rows
   int32_t G;
   int64_t M;
+  int64_t group_rows;     // seg == nullptr: G groups of group_rows rows each (> 0), or one
+                          // group of M rows (0)
   int32_t N;              // output columns
   int32_t K;              // contraction length, a multiple of BK
   void* C;                // [rows, N] output (row stride N)
   const float* bias;      // EPI_F32_BIAS: [N] or nullptr
   int32_t n_group;        // tile order: column tiles per group (<= 0: all columns of a row tile)
   int32_t m_chunk;        // tile order: row tiles per chunk (<= 0: all row tiles of a group)
+  float alpha, beta;      // EPI_AXPBY: C = alpha * (A B^T) + beta * D
+  const void* D;          // EPI_AXPBY: [rows, N], same layout and type as C
 };
 
 // Per element type: how one wave multiplies a 32x32 block over 16 k values.
@@ -133,6 +137,19 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((const MOE_LDS char*)p);
 }
 
+// Load 4 consecutive values (8 bytes of bf16 or 16 bytes of float) as floats.
+__device__ __forceinline__ void load4(const bf16* p, float* v) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+  const bf16x4 q = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = static_cast<float>(q[i]);
+}
+__device__ __forceinline__ void load4(const float* p, float* v) {
+  const f32x4 q = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = q[i];
+}
+
 // Store 4 consecutive outputs (8 bytes of bf16 or 16 bytes of float).
 __device__ __forceinline__ void store4(bf16* p, const float* v) {
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
@@ -190,7 +207,7 @@ struct GemmTile {
 
 // Exclusive prefix over groups of the number of tiles each owns, into tstart[0..G].
 template <int BM, int NTHREADS>
-__device__ void build_tile_prefix(const int32_t* seg, int G, int64_t M, int ntn, int* tstart) {
+__device__ void build_tile_prefix(const int32_t* seg, int G, int64_t M, int64_t group_rows, int ntn, int* tstart) {
   const int tid = threadIdx.x;
   if (tid < 64) {
     const int lane = tid;
@@ -198,7 +215,7 @@ __device__ void build_tile_prefix(const int32_t* seg, int G, int64_t M, int ntn,
     const int lo = min(G, lane * per), hi = min(G, lo + per);
     int sum = 0;
     for (int g = lo; g < hi; ++g) {
-      const int64_t rows = seg ? (int64_t)seg[g + 1] - seg[g] : M;
+      const int64_t rows = seg ? (int64_t)seg[g + 1] - seg[g] : (group_rows > 0 ? group_rows : M);
       sum += (int)((rows + BM - 1) / BM) * ntn;
     }
     int incl = sum;
@@ -210,7 +227,7 @@ __device__ void build_tile_prefix(const int32_t* seg, int G, int64_t M, int ntn,
     int run = incl - sum;
     for (int g = lo; g < hi; ++g) {
       tstart[g] = run;
-      const int64_t rows = seg ? (int64_t)seg[g + 1] - seg[g] : M;
+      const int64_t rows = seg ? (int64_t)seg[g + 1] - seg[g] : (group_rows > 0 ? group_rows : M);
       run += (int)((rows + BM - 1) / BM) * ntn;
     }
     if (lane == 63) tstart[G] = incl;
@@ -242,10 +259,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  const int G = p.seg ? p.G : 1;
+  const int G = (p.seg || p.group_rows > 0) ? p.G : 1;
   const int ntn = (p.N + NOUT - 1) / NOUT;
-  build_tile_prefix<BM, NT>(p.seg, G, p.M, ntn, tstart);
-  const int total = __builtin_amdgcn_readfirstlane(tstart[G]);
+  // equal groups (a batch of matrices): group g owns tiles [g * per_g, (g+1) * per_g)
+  const bool uniform = p.seg == nullptr;
+  const int per_g = uniform ? (int)((p.group_rows > 0 ? p.group_rows : p.M) + BM - 1) / BM * ntn : 0;
+  if (!uniform) build_tile_prefix<BM, NT>(p.seg, G, p.M, p.group_rows, ntn, tstart);
+  const int total = uniform ? G * per_g : __builtin_amdgcn_readfirstlane(tstart[G]);
   const int K = p.K;
   const int nk = K / BK;
   const T* __restrict__ Abase = static_cast<const T*>(p.A);
@@ -256,16 +276,22 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     int64_t m0;
   };
   auto locate = [&](int tile) -> TileInfo {
-    int lo = 0, hi = G;                      // largest g with tstart[g] <= tile
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (tstart[mid] <= tile) lo = mid; else hi = mid;
-    }
     TileInfo t;
-    t.g = __builtin_amdgcn_readfirstlane(lo);
-    const int local = tile - __builtin_amdgcn_readfirstlane(tstart[t.g]);
-    const int64_t seg_lo = p.seg ? (int64_t)p.seg[t.g] : 0;
-    const int64_t seg_hi = p.seg ? (int64_t)p.seg[t.g + 1] : p.M;
+    int local;
+    if (uniform) {
+      t.g = tile / per_g;
+      local = tile - t.g * per_g;
+    } else {
+      int lo = 0, hi = G;                    // largest g with tstart[g] <= tile
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tstart[mid] <= tile) lo = mid; else hi = mid;
+      }
+      t.g = __builtin_amdgcn_readfirstlane(lo);
+      local = tile - __builtin_amdgcn_readfirstlane(tstart[t.g]);
+    }
+    const int64_t seg_lo = p.seg ? (int64_t)p.seg[t.g] : (int64_t)t.g * p.group_rows;
+    const int64_t seg_hi = p.seg ? (int64_t)p.seg[t.g + 1] : (p.group_rows > 0 ? seg_lo + p.group_rows : p.M);
     // Within a group the tiles run in chunks of SM row tiles; inside a chunk, in
     // column groups of NG column tiles; inside a column group, row tile by row
     // tile.  Consecutive tiles then share A rows (same row tile) and B columns
@@ -445,7 +471,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
             }
           }
       }
-    } else if constexpr (NT == 512 && Cfg::WTM == 64 && 8 * kEpiWaveBytes <= Cfg::kStageBytes) {
+    } else if constexpr (EPI != EPI_AXPBY && NT == 512 && Cfg::WTM == 64 && 8 * kEpiWaveBytes <= Cfg::kStageBytes) {
       // Staged through LDS (wbuf: this wave's 32 rows x 144 bytes, which nothing
       // else touches until the next barrier).  Per round
       // (one row block mi, 128 bytes of output columns) it parks its values there
@@ -517,12 +543,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
             const int col = en0 + wn * CW + ni * 32 + 8 * q + h4;
             if (col < p.N) {
               float v[4];
+              float dv[4] = {0.f, 0.f, 0.f, 0.f};
+              if constexpr (EPI == EPI_AXPBY)
+                load4(static_cast<const T*>(p.D) + (em0 + r) * (int64_t)p.N + col, dv);
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 if constexpr (EPI == EPI_SWIGLU) {
                   const float gv = acc[mi][ni][4 * q + i];
                   const float uv = acc[mi][ni + NI / 2][4 * q + i];
                   v[i] = gv / (1.0f + __expf(-gv)) * uv;
+                } else if constexpr (EPI == EPI_AXPBY) {
+                  v[i] = p.alpha * acc[mi][ni][4 * q + i] + p.beta * dv[i];
                 } else {
                   v[i] = acc[mi][ni][4 * q + i];
                 }

@@ -32,6 +32,14 @@ hipError_t launch_grouped_ffn(int dtype, int64_t n_max, int64_t d, int64_t E, in
                               const void* w_up, const void* w_down, void* y_perm, void* h,
                               int num_cu, hipStream_t stream);
 
+// Muon's Newton-Schulz orthogonalisation of n bf16 matrices [R, C] (R, C multiples
+// of 64): g in, x out; xw [n, R', C'], xt0 and xt1 [n, C', R'], A and B [n, R', R']
+// (R' = min(R, C), C' = max(R, C)) and partial [n * kNormBlocks] are scratch.
+constexpr int kNormBlocks = 64;
+hipError_t launch_newton_schulz(int64_t n, int64_t R, int64_t C, int64_t steps, float a, float b, float c,
+                                float eps, const void* g, void* x, void* xw, void* xt0, void* xt1, void* A,
+                                void* B, float* partial, int num_cu, hipStream_t stream);
+
 // Weighted un-permute: y[t] = sum_j w[t,j] * y_perm[slot_row[t,j]].
 hipError_t launch_combine(int dtype, int64_t T, int64_t d, int64_t k, const void* y_perm,
                           const int32_t* slot_row, const float* w, void* y, hipStream_t stream);

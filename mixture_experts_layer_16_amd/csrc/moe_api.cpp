@@ -178,6 +178,41 @@ moe_status moe_grouped_ffn(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_d
                                             y_perm, ws, ncu, static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_newton_schulz(int64_t n, int64_t R, int64_t C, moe_dtype dtype, int64_t steps, float a, float b,
+                             float c, float eps, const void* g, void* x, void* ws, size_t* ws_bytes, void* stream) {
+  if (n <= 0 || R <= 0 || C <= 0 || steps < 0 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_BF16 || R % 64 != 0 || C % 64 != 0 || R > kMaxDim || C > kMaxDim || n > (int64_t(1) << 16) ||
+      R * C >= kIdxLimit || n * (R / 256 + 1) * (C / 256 + 1) >= kIdxLimit)
+    return MOE_ERR_UNSUPPORTED;
+  const size_t per = (size_t)R * (size_t)C * 2, sq = (size_t)(R < C ? R : C) * (size_t)(R < C ? R : C) * 2;
+  Carver c0(nullptr);
+  c0.take(n * per);                               // X, wide orientation
+  c0.take(n * per);                               // X^T, two of them
+  c0.take(n * per);
+  c0.take(n * sq);                                // A = X X^T
+  c0.take(n * sq);                                // B = b A + c A A
+  c0.take((size_t)n * moe::kNormBlocks * 4);      // partial sums of squares
+  const size_t need = c0.used;
+  if (ws == nullptr && ws_bytes != nullptr) {
+    *ws_bytes = need;
+    return MOE_OK;
+  }
+  if (!ok16(g) || !ok16(x)) return MOE_ERR_INVALID_ARG;
+  moe_status st = MOE_OK;
+  if (workspace_step(ws, ws_bytes, need, &st)) return st;
+  int ncu = 0;
+  if ((st = num_cu(&ncu)) != MOE_OK) return st;
+  Carver cv(ws);
+  void* xw = cv.take(n * per);
+  void* xt0 = cv.take(n * per);
+  void* xt1 = cv.take(n * per);
+  void* A = cv.take(n * sq);
+  void* B = cv.take(n * sq);
+  float* partial = static_cast<float*>(cv.take((size_t)n * moe::kNormBlocks * 4));
+  return hip_status(moe::launch_newton_schulz(n, R, C, steps, a, b, c, eps, g, x, xw, xt0, xt1, A, B, partial, ncu,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_combine(int64_t T, int64_t d, int64_t k, moe_dtype dtype, const void* y_perm,
                        const int32_t* slot_row, const float* topk_w, void* y, void* stream) {
   if (T <= 0 || d <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;

@@ -1,0 +1,171 @@
+// Muon's Newton-Schulz orthogonalisation of a batch of whole matrices.
+//
+// Muon orthogonalises every update with a few Newton-Schulz iterations over the
+// whole matrix, and whole experts are placed on one rank so each rank runs them
+// on complete expert matrices without communication ("FlexShard: communication-
+// free Muon" in "Training a 1T-Parameter MoE on EU public infrastructure with
+// PyTorch and TorchTitan").  The iteration is Muon's quintic, on the wide
+// orientation of each matrix (a tall one is transposed first and back at the
+// end):
+//     X = G / (||G||_F + eps);   repeat: A = X X^T,  B = b A + c A A,  X = a X + B X
+//
+// Layout and kernels (bf16 storage, fp32 accumulation):
+//   * sum of squares per matrix: kNormBlocks partial sums, each over a fixed
+//     contiguous chunk, then every consumer adds the partials in one fixed order
+//     (deterministic, no atomics);
+//   * init: X0 scaled and cast, written both as Xw [R', C'] (wide) and as its
+//     transpose Xt [C', R'] through a 64 x 64 LDS tile;
+//   * per step, three launches of the grouped NT GEMM with one group per matrix:
+//       A  = Xw Xw^T                   (K = C')
+//       B  = c (A A^T) + b A           (K = R'; A is symmetric, so A A^T = A A)
+//       Xt' = (Xt B^T) + a Xt          (K = R'; B is symmetric, so Xt B^T = (B Xw)^T)
+//     then Xt' is transposed back into Xw for the next step's A (the product
+//     forms of the GEMM read both operands along K, so X X^T needs X's rows and
+//     B X needs X^T's rows).  The last step writes the result in the caller's
+//     orientation straight into the output.
+#include "common.h"
+#include "gemm_tile.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kTile = 64;
+
+// partial[m * kNormBlocks + b] = sum of squares of chunk b of matrix m
+__global__ __launch_bounds__(256) void ns_sumsq_kernel(const bf16* __restrict__ g, int64_t per, float* __restrict__ partial) {
+  __shared__ float wsum[4];
+  const int m = blockIdx.y, b = blockIdx.x;
+  const int64_t chunk = (per + kNormBlocks - 1) / kNormBlocks;
+  const int64_t lo = min<int64_t>(per, (int64_t)b * chunk), hi = min<int64_t>(per, lo + chunk);
+  const bf16* p = g + (int64_t)m * per;
+  float s = 0.f;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
+    const float v = static_cast<float>(p[i]);
+    s = fmaf(v, v, s);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[(int64_t)m * kNormBlocks + b] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+}
+
+// scale = 1 / (sqrt(sum of the partials in order) + eps); out_same = scale * G (G's
+// orientation), out_t = its transpose.  One 64 x 64 tile of one matrix per block.
+__global__ __launch_bounds__(256) void ns_init_kernel(const bf16* __restrict__ g, int R, int C,
+                                                      const float* __restrict__ partial, float eps,
+                                                      bf16* __restrict__ out_same, bf16* __restrict__ out_t) {
+  __shared__ float tile[kTile][kTile + 1];
+  const int m = blockIdx.z;
+  float ss = 0.f;
+  for (int i = 0; i < kNormBlocks; ++i) ss += partial[(int64_t)m * kNormBlocks + i];
+  const float scale = 1.0f / (sqrtf(ss) + eps);
+  const int64_t per = (int64_t)R * C;
+  const bf16* G = g + m * per;
+  bf16* S = out_same + m * per;
+  bf16* Tt = out_t + m * per;
+  const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < kTile; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    const float v = static_cast<float>(G[(int64_t)r * C + c]) * scale;
+    tile[i][tx] = v;
+    S[(int64_t)r * C + c] = static_cast<bf16>(v);
+  }
+  __syncthreads();
+  for (int i = ty; i < kTile; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    Tt[(int64_t)c * R + r] = static_cast<bf16>(tile[tx][i]);
+  }
+}
+
+// dst[m] = src[m]^T for [rows, cols] bf16 matrices; one 64 x 64 tile per block.
+__global__ __launch_bounds__(256) void ns_transpose_kernel(const bf16* __restrict__ src, int rows, int cols,
+                                                           bf16* __restrict__ dst) {
+  __shared__ bf16 tile[kTile][kTile + 2];
+  const int64_t per = (int64_t)rows * cols;
+  const bf16* S = src + blockIdx.z * per;
+  bf16* D = dst + blockIdx.z * per;
+  const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < kTile; i += 4) tile[i][tx] = S[(int64_t)(r0 + i) * cols + c0 + tx];
+  __syncthreads();
+  for (int i = ty; i < kTile; i += 4) D[(int64_t)(c0 + i) * rows + r0 + tx] = tile[tx][i];
+}
+
+GemmArgs batch_gemm(const bf16* A, const bf16* B, int64_t b_stride, int n, int64_t rows, int N, int K, bf16* C) {
+  GemmArgs a{};
+  a.A = A;
+  a.a_rows = nullptr;
+  a.B0 = B;
+  a.B1 = nullptr;
+  a.b_stride = b_stride;
+  a.seg = nullptr;
+  a.G = n;
+  a.M = (int64_t)n * rows;
+  a.group_rows = rows;
+  a.N = N;
+  a.K = K;
+  a.C = C;
+  a.bias = nullptr;
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_newton_schulz(int64_t n, int64_t R, int64_t C, int64_t steps, float a, float b, float c,
+                                float eps, const void* g, void* x, void* xw, void* xt0, void* xt1, void* A,
+                                void* B, float* partial, int num_cu, hipStream_t stream) {
+  const bool tall = R > C;
+  const int64_t Rw = tall ? C : R, Cw = tall ? R : C;   // wide orientation
+  const int64_t per = R * C;
+  const bf16* G = static_cast<const bf16*>(g);
+  bf16* X = static_cast<bf16*>(x);
+  bf16* Xw = static_cast<bf16*>(xw);
+  bf16* Xt[2] = {static_cast<bf16*>(xt0), static_cast<bf16*>(xt1)};
+  bf16* Ab = static_cast<bf16*>(A);
+  bf16* Bb = static_cast<bf16*>(B);
+
+  hipLaunchKernelGGL(ns_sumsq_kernel, dim3(kNormBlocks, (unsigned)n), dim3(256), 0, stream, G, per, partial);
+  // X0 in G's orientation and transposed; which one is the wide one depends on tall
+  bf16* same = steps == 0 ? X : (tall ? Xt[0] : Xw);
+  bf16* trans = tall ? Xw : Xt[0];
+  hipLaunchKernelGGL(ns_init_kernel, dim3((unsigned)(C / kTile), (unsigned)(R / kTile), (unsigned)n), dim3(256), 0,
+                     stream, G, (int)R, (int)C, partial, eps, same, trans);
+  if (steps == 0) return hipGetLastError();
+
+  constexpr int BK = 64, ST = 2, WM = 4, WN = 2;
+  int cur = 0;
+  for (int64_t s = 0; s < steps; ++s) {
+    const bool last = s + 1 == steps;
+    // A = Xw Xw^T
+    GemmArgs p1 = batch_gemm(Xw, Xw, Rw * Cw, (int)n, Rw, (int)Rw, (int)Cw, Ab);
+    hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, BK, WM, WN, ST, EPI_STORE, 1>), dim3(num_cu),
+                       dim3(WM * WN * 64), 0, stream, p1);
+    // B = c (A A^T) + b A
+    GemmArgs p2 = batch_gemm(Ab, Ab, Rw * Rw, (int)n, Rw, (int)Rw, (int)Rw, Bb);
+    p2.alpha = c;
+    p2.beta = b;
+    p2.D = Ab;
+    hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, BK, WM, WN, ST, EPI_AXPBY, 1>), dim3(num_cu),
+                       dim3(WM * WN * 64), 0, stream, p2);
+    // Xt' = Xt B^T + a Xt; for a tall matrix Xt is the caller's orientation
+    bf16* out = (last && tall) ? X : Xt[cur ^ 1];
+    GemmArgs p3 = batch_gemm(Xt[cur], Bb, Rw * Rw, (int)n, Cw, (int)Rw, (int)Rw, out);
+    p3.alpha = 1.0f;
+    p3.beta = a;
+    p3.D = Xt[cur];
+    hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, BK, WM, WN, ST, EPI_AXPBY, 1>), dim3(num_cu),
+                       dim3(WM * WN * 64), 0, stream, p3);
+    if (last && tall) break;
+    // Xw = Xt'^T (the result itself on the last step of a wide matrix)
+    hipLaunchKernelGGL(ns_transpose_kernel, dim3((unsigned)(Rw / kTile), (unsigned)(Cw / kTile), (unsigned)n),
+                       dim3(256), 0, stream, out, (int)Cw, (int)Rw, last ? X : Xw);
+    cur ^= 1;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

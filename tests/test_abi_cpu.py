@@ -185,3 +185,35 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         B.lib()
+
+
+# ---- Newton-Schulz ------------------------------------------------------------
+
+def ns(n=2, R=128, C=192, dt=1, steps=5, eps=1e-7, g=P, x=P, ws=P, nbytes=1 << 30):
+    nb = ctypes.c_size_t(nbytes)
+    return B.lib().moe_newton_schulz(n, R, C, dt, steps, 3.4445, -4.775, 2.0315, eps, g, x, ws, ctypes.byref(nb),
+                                     None)
+
+
+def ns_ws(n, R, C):
+    per, sq = R * C * 2, min(R, C) ** 2 * 2
+    return 3 * ru(n * per) + 2 * ru(n * sq) + ru(n * 64 * 4)
+
+
+@pytest.mark.parametrize("n,R,C", [(1, 64, 64), (3, 128, 320), (2, 320, 128), (288, 1792, 6144)])
+def test_newton_schulz_workspace_query(n, R, C):
+    nb = ctypes.c_size_t(12345)
+    st = B.lib().moe_newton_schulz(n, R, C, 1, 5, 3.4445, -4.775, 2.0315, 1e-7, P, P, None, ctypes.byref(nb), None)
+    assert st == OK and nb.value == ns_ws(n, R, C)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), INVALID), (dict(R=0), INVALID), (dict(C=-64), INVALID), (dict(steps=-1), INVALID),
+    (dict(eps=-1.0), INVALID), (dict(eps=float("nan")), INVALID),
+    (dict(R=100), UNSUPPORTED), (dict(C=96), UNSUPPORTED), (dict(dt=0), UNSUPPORTED), (dict(dt=5), UNSUPPORTED),
+    (dict(n=1 << 17), UNSUPPORTED),
+    (dict(g=None), INVALID), (dict(x=P_MIS), INVALID), (dict(nbytes=1000), WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x10010)), INVALID),
+])
+def test_newton_schulz_argument_errors(kw, status):
+    assert ns(**kw) == status
