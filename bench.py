@@ -11,6 +11,11 @@ GEMM launches, timed together with HIP events on the launch stream) against
 the bf16 dense MFMA peak; `stages_ms` gives each step's average duration from
 a second, stage-by-stage pass; `cpu_baseline` times the float64 CPU oracle on a
 bounded slice of the same workload.
+
+`--path newton_schulz` measures the next row instead: Muon's Newton-Schulz
+orthogonalisation of whole expert matrices (one step = the gate, up and down
+matrices of the 96 experts one expert-parallel rank owns, five quintic steps
+each), on the same contract.
 """
 from __future__ import annotations
 
@@ -35,6 +40,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="page_seq64k_skewed")
+    ap.add_argument("--path", default="layer", choices=["layer", "newton_schulz"],
+                    help="layer: the MoE layer forward (default); newton_schulz: Muon's orthogonalisation "
+                         "of whole expert matrices")
+    ap.add_argument("--ns-experts", type=int, default=96,
+                    help="newton_schulz: experts whose gate, up and down matrices one step orthogonalises")
     ap.add_argument("--cpu-tokens", type=int, default=512,
                     help="tokens of the workload the CPU oracle runs on (0 = skip)")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -144,6 +154,68 @@ def cpu_baseline(torch, inp, wl, n_tokens):
                       f"{threads} BLAS threads of {os.cpu_count()} host CPUs"}
 
 
+NS_METRIC = "Muon Newton-Schulz expert matrices/s (5 quintic steps, d6144 x F1792, bf16)"
+
+
+def ns_flops(R, C, steps):
+    """Algorithmic FLOPs of the iteration on one R x C matrix (wide side C):
+    X X^T, A A and B X per step."""
+    r, c = min(R, C), max(R, C)
+    return steps * (2 * r * r * c + 2 * r * r * r + 2 * r * r * c)
+
+
+def bench_newton_schulz(args, torch, B):
+    """One step: the gate and up matrices [F, d] and the down matrices [d, F] of
+    args.ns_experts experts (two calls: one per orientation)."""
+    import numpy as np
+    d, F, steps = 6144, 1792, 5
+    n = args.ns_experts
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    wide = torch.randn(2 * n, F, d, generator=g, device="cuda:0").to(torch.bfloat16)
+    tall = torch.randn(n, d, F, generator=g, device="cuda:0").to(torch.bfloat16)
+    calls = [B.NewtonSchulz(wide, steps), B.NewtonSchulz(tall, steps)]
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        for c in calls:
+            c()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    mats = 3 * n
+    flops = mats * ns_flops(F, d, steps)
+    tflops = flops / (ms / 1e3) / 1e12
+    out = {
+        "metric": NS_METRIC, "value": round(mats / (ms / 1e3), 2), "unit": "matrices/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random bf16 matrices of the page's expert shapes)",
+        "config": {"workload": f"muon_ns_{n}_experts", "matrices": mats, "wide": [2 * n, F, d],
+                   "tall": [n, d, F], "ns_steps": steps},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "moe_newton_schulz (3 batched GEMM launches + 1 transpose per step)",
+                     "flops_per_launch": flops, "ms_per_launch": round(ms, 3)},
+    }
+    if args.cpu_tokens > 0:
+        from threadpoolctl import threadpool_info
+        from oracle import muon_oracle as orc
+        G = wide[0].float().cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        orc.newton_schulz(G, steps=steps)
+        dt = time.perf_counter() - t0
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        out["cpu_baseline"] = {"value": round(1.0 / dt, 4), "unit": "matrices/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"one {F}x{d} matrix, float64 oracle, {steps} steps: {dt:.1f} s on "
+                                         f"{threads} BLAS threads of {os.cpu_count()} host CPUs"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -156,8 +228,11 @@ def main():
     from mixture_experts_layer_16_amd import binding as B
     from mixture_experts_layer_16_amd import workloads as W
 
-    wl = W.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
+    if args.path == "newton_schulz":
+        bench_newton_schulz(args, torch, B)
+        return
+    wl = W.WORKLOADS[args.workload]
     if args.traffic_probe:
         traffic_probe(torch, B, W, wl)
         return
