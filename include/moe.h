@@ -160,6 +160,33 @@ moe_status moe_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
                              int32_t* offsets_out, void* ws, size_t* ws_bytes, void* stream);
 
 /*
+ * moe_grouped_ffn_backward: gradients of the grouped SwiGLU FFN (the layer
+ * backward's matrix products; the pages' workload is pre-training, "Training a
+ * 1T-Parameter MoE on EU public infrastructure with PyTorch and TorchTitan").
+ * For expert e and its rows X (as in moe_grouped_ffn) with output gradient dY:
+ *   dH = dY W_d, S = silu(X W_g^T), U = X W_u^T, H = S U,
+ *   dU = dH S, dG = dH U silu'(X W_g^T),
+ *   dX = dG W_g + dU W_u,  dW_d = dY^T H,  dW_g = dG^T X,  dW_u = dU^T X.
+ * G and U are recomputed (nothing from the forward is needed but its inputs).
+ *   n_max, d, E, F, x_in, n_in, a_rows, offsets, w_gate, w_up, w_down: as in
+ *                        moe_grouped_ffn (dtype MOE_BF16 only)
+ *   dy_perm  [n_max,d] bf16    dY, rows grouped by expert (rows offsets[E].. unused)
+ *   dx_perm  [n_max,d] bf16    out: dX (first offsets[E] rows written)
+ *   dw_gate, dw_up [E,F,d] f32, dw_down [E,d,F] f32   out; zero for an expert with
+ *                        no rows
+ *   ws: query with ws == NULL (holds transposed weights, dH in float32, dG|dU,
+ *       H and transposed activations: about 3 E d F + n_max (4 + 2 + 2 + 2 + ...) F
+ *       + 2 (d + 3 F) (n_max + 63 E) elements).
+ * Errors as moe_grouped_ffn; a dtype other than MOE_BF16 is MOE_ERR_UNSUPPORTED.
+ */
+moe_status moe_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_dtype dtype,
+                                    const void* x_in, int64_t n_in, const int32_t* a_rows,
+                                    const int32_t* offsets, const void* w_gate, const void* w_up,
+                                    const void* w_down, const void* dy_perm, void* dx_perm,
+                                    float* dw_gate, float* dw_up, float* dw_down,
+                                    void* ws, size_t* ws_bytes, void* stream);
+
+/*
  * moe_newton_schulz: Muon's orthogonalisation of a batch of whole matrices
  * ("Training a 1T-Parameter MoE on EU public infrastructure with PyTorch and
  * TorchTitan", section "FlexShard: communication-free Muon": a few

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
-EXPORTS = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_newton_schulz")
+EXPORTS = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_newton_schulz",
+           "moe_grouped_ffn_backward")
 
 
 class MoEError(RuntimeError):
@@ -40,6 +41,8 @@ _SIGS = {
     "moe_layer_forward": [_i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                           _vp, _vp, _szp, _vp],
     "moe_newton_schulz": [_i64, _i64, _i64, _int, _i64, _f32, _f32, _f32, _f32, _vp, _vp, _vp, _szp, _vp],
+    "moe_grouped_ffn_backward": [_i64, _i64, _i64, _i64, _int, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _szp, _vp],
 }
 
 MUON_COEFFS = (3.4445, -4.7750, 2.0315)
@@ -159,6 +162,38 @@ def moe_combine(y_perm, slot_row, topk_w, out=None):
     _check("moe_combine", lib().moe_combine(T, d, k, dtype_code(y_perm.dtype), _p(y_perm), _p(slot_row),
                                             _p(topk_w), _p(y), _stream(y_perm.device)))
     return y
+
+
+class GroupedFfnBackward:
+    """moe_grouped_ffn_backward with its outputs and workspace allocated once.
+    x_in is x_perm, or (a_rows given) the token matrix read through a_rows."""
+
+    def __init__(self, x_in, offsets, w_gate, w_up, w_down, dy_perm, a_rows=None):
+        E, F, d = w_gate.shape
+        n_max = dy_perm.shape[0]
+        dev = dy_perm.device
+        n_in = x_in.shape[0] if a_rows is not None else 0
+        self.t = (x_in, offsets, w_gate, w_up, w_down, dy_perm, a_rows)
+        self.dx = torch.empty(n_max, d, dtype=dy_perm.dtype, device=dev)
+        self.dwg = torch.empty(E, F, d, dtype=torch.float32, device=dev)
+        self.dwu = torch.empty(E, F, d, dtype=torch.float32, device=dev)
+        self.dwd = torch.empty(E, d, F, dtype=torch.float32, device=dev)
+        self.head = (n_max, d, E, F, dtype_code(dy_perm.dtype))
+        self.mid = (_p(x_in), n_in, _p(a_rows), _p(offsets), _p(w_gate), _p(w_up), _p(w_down), _p(dy_perm),
+                    _p(self.dx), _p(self.dwg), _p(self.dwu), _p(self.dwd))
+        self.ws = _ws(_query("moe_grouped_ffn_backward", *self.head, *self.mid), dev)
+
+    def __call__(self):
+        n = ctypes.c_size_t(self.ws.numel())
+        _check("moe_grouped_ffn_backward",
+               lib().moe_grouped_ffn_backward(*self.head, *self.mid, _p(self.ws), ctypes.byref(n),
+                                              _stream(self.dx.device)))
+        return self.dx, self.dwg, self.dwu, self.dwd
+
+
+def moe_grouped_ffn_backward(x_in, offsets, w_gate, w_up, w_down, dy_perm, a_rows=None):
+    """(dx_perm, dW_gate, dW_up, dW_down) of the grouped SwiGLU FFN."""
+    return GroupedFfnBackward(x_in, offsets, w_gate, w_up, w_down, dy_perm, a_rows)()
 
 
 class NewtonSchulz:

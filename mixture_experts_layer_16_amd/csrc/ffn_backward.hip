@@ -1,0 +1,197 @@
+// Backward pass of the grouped SwiGLU expert FFN.
+//
+// The pages' workload is pre-training ("Training a 1T-Parameter MoE on EU public
+// infrastructure with PyTorch and TorchTitan"), so every step also runs the
+// layer backward.  For expert e with rows X (token rows, read in place through
+// the gather map or from x_perm) and output gradient dY (rows of dy_perm):
+//     dH = dY W_d,   S = silu(X W_g^T),  U = X W_u^T,  H = S U
+//     dU = dH S,     dG = dH U silu'(X W_g^T)
+//     dX = dG W_g + dU W_u
+//     dW_d = dY^T H,   dW_g = dG^T X,   dW_u = dU^T X
+//
+// Everything runs on the grouped NT GEMM (C = A B^T, both operands read along
+// the contraction):
+//   * dH = dY (W_d^T)^T and dX = [dG | dU] [W_g^T ; W_u^T]^T read transposed
+//     copies of the weights ([E, F, d] and [E, d, 2F], made here, bandwidth-
+//     bound), in float32 (dH) and the I/O type (dX);
+//   * G and U are recomputed by the gate/up GEMM, whose epilogue turns them and
+//     dH into dG, dU (one [n, 2F] buffer) and H;
+//   * the weight gradients contract over each expert's rows: the activations
+//     are transposed into a layout where expert e owns columns
+//     [poff[e], poff[e+1]) (its row count rounded up to 64, the gap zero-filled),
+//     and one GEMM per gradient runs with one group per expert whose k range
+//     is that column range, every group reading the same operand rows.  An
+//     expert with no rows gets a zero gradient.
+#include "common.h"
+#include "gemm_tile.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kTile = 64;
+
+// poff[e] = sum over e' < e of the row count of e' rounded up to 64 (one block).
+__global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __restrict__ offsets, int E,
+                                                           int32_t* __restrict__ poff) {
+  __shared__ int wsum[16];
+  const int e = threadIdx.x;
+  const int v = e < E ? (offsets[e + 1] - offsets[e] + 63) / 64 * 64 : 0;
+  const int lane = e & 63, wv = e >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < wv; ++i) before += wsum[i];
+  if (e < E) poff[e] = before + incl - v;
+  if (e == E - 1) poff[E] = before + incl;
+}
+
+// dst[c, p] (row stride ld_dst) for padded column p of expert e = src row
+// offsets[e] + (p - poff[e]) (through rows[] when given), columns col0 + c of the
+// source (row stride ld_src); zero past the expert's rows.  One 64 x 64 tile per
+// block; blocks past poff[E] have nothing to do.
+template <typename T>
+__global__ __launch_bounds__(256) void pad_transpose_kernel(const T* __restrict__ src, int64_t ld_src, int col0,
+                                                            const int32_t* __restrict__ rows,
+                                                            const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ poff, int E,
+                                                            T* __restrict__ dst, int64_t ld_dst) {
+  __shared__ T tile[kTile][kTile + 2];
+  const int p0 = blockIdx.x * kTile;
+  if (p0 >= poff[E]) return;
+  int lo = 0, hi = E;                       // largest e with poff[e] <= p0
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (poff[mid] <= p0) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int r0 = p0 - poff[e];
+  const int n_e = offsets[e + 1] - offsets[e];
+  const int c0 = blockIdx.y * kTile;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int j = ty; j < kTile; j += 4) {
+    T v = static_cast<T>(0.0f);
+    if (r0 + j < n_e) {
+      const int64_t sr = offsets[e] + r0 + j;
+      const int64_t row = rows ? (int64_t)rows[sr] : sr;
+      v = src[row * ld_src + col0 + c0 + tx];
+    }
+    tile[j][tx] = v;
+  }
+  __syncthreads();
+  for (int i = ty; i < kTile; i += 4) dst[(int64_t)(c0 + i) * ld_dst + p0 + tx] = tile[tx][i];
+}
+
+// dst[b][c * ld_dst + coff + r] = src[b][r * cols + c] for b < batch: transposes
+// of [rows, cols] matrices into column range [coff, coff + rows) of [cols, ld_dst].
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_into_kernel(const T* __restrict__ src, int rows, int cols,
+                                                             T* __restrict__ dst, int64_t ld_dst, int coff,
+                                                             int64_t dst_batch) {
+  __shared__ T tile[kTile][kTile + 2];
+  const T* S = src + (int64_t)blockIdx.z * rows * cols;
+  T* D = dst + (int64_t)blockIdx.z * dst_batch;
+  const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < kTile; i += 4) tile[i][tx] = S[(int64_t)(r0 + i) * cols + c0 + tx];
+  __syncthreads();
+  for (int i = ty; i < kTile; i += 4) D[(int64_t)(c0 + i) * ld_dst + coff + r0 + tx] = tile[tx][i];
+}
+
+GemmArgs args_grouped(const void* A, const int32_t* a_rows, const void* B0, const void* B1, int64_t b_stride,
+                      const int32_t* seg, int G, int64_t M, int N, int K, void* C) {
+  GemmArgs a{};
+  a.A = A;
+  a.a_rows = a_rows;
+  a.B0 = B0;
+  a.B1 = B1;
+  a.b_stride = b_stride;
+  a.seg = seg;
+  a.G = G;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.C = C;
+  return a;
+}
+
+template <typename T, int BK, int EPI>
+void gemm(const GemmArgs& a, int num_cu, hipStream_t s) {
+  hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, 4, 2, 2, EPI, 1>), dim3(num_cu), dim3(512), 0, s, a);
+}
+
+}  // namespace
+
+hipError_t launch_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_in,
+                                       const int32_t* a_rows, const int32_t* offsets, const void* w_gate,
+                                       const void* w_up, const void* w_down, const void* dy_perm, void* dx_perm,
+                                       float* dw_gate, float* dw_up, float* dw_down, const FfnBackwardScratch& w,
+                                       int num_cu, hipStream_t s) {
+  typedef bf16 T;
+  constexpr int BK = 64;
+  const int64_t np = w.n_pad;   // columns of the padded transposed layouts
+  const T* Wg = static_cast<const T*>(w_gate);
+  const T* Wu = static_cast<const T*>(w_up);
+  const T* Wd = static_cast<const T*>(w_down);
+
+  // padded expert column ranges; transposed weights
+  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(1024), 0, s, offsets, (int)E, w.poff);
+  hipLaunchKernelGGL((transpose_into_kernel<T>), dim3((unsigned)(F / kTile), (unsigned)(d / kTile), (unsigned)E),
+                     dim3(256), 0, s, Wd, (int)d, (int)F, static_cast<T*>(w.wd_t), d, 0, F * d);
+  hipLaunchKernelGGL((transpose_into_kernel<T>), dim3((unsigned)(d / kTile), (unsigned)(F / kTile), (unsigned)E),
+                     dim3(256), 0, s, Wg, (int)F, (int)d, static_cast<T*>(w.wgu_t), 2 * F, 0, d * 2 * F);
+  hipLaunchKernelGGL((transpose_into_kernel<T>), dim3((unsigned)(d / kTile), (unsigned)(F / kTile), (unsigned)E),
+                     dim3(256), 0, s, Wu, (int)F, (int)d, static_cast<T*>(w.wgu_t), 2 * F, (int)F, d * 2 * F);
+
+  // dH = dY W_d (float32)
+  GemmArgs a1 = args_grouped(dy_perm, nullptr, w.wd_t, nullptr, F * d, offsets, (int)E, n_max, (int)F, (int)d,
+                             w.dh);
+  gemm<T, BK, EPI_F32_BIAS>(a1, num_cu, s);
+  // recompute G, U; dG | dU and H
+  GemmArgs a2 = args_grouped(x_in, a_rows, w_gate, w_up, F * d, offsets, (int)E, n_max, (int)F, (int)d, w.dgu);
+  a2.D = w.dh;
+  a2.C2 = w.h;
+  a2.ldc = 2 * F;
+  gemm<T, BK, EPI_SWIGLU_BWD>(a2, num_cu, s);
+  // dX = [dG | dU] [W_g^T ; W_u^T]^T
+  GemmArgs a3 = args_grouped(w.dgu, nullptr, w.wgu_t, nullptr, d * 2 * F, offsets, (int)E, n_max, (int)d,
+                             (int)(2 * F), dx_perm);
+  gemm<T, BK, EPI_STORE>(a3, num_cu, s);
+
+  // transposed, padded activations for the weight gradients
+  const dim3 gd((unsigned)(np / kTile), (unsigned)(d / kTile)), gf((unsigned)(np / kTile), (unsigned)(F / kTile));
+  hipLaunchKernelGGL((pad_transpose_kernel<T>), gd, dim3(256), 0, s, static_cast<const T*>(x_in), d, 0, a_rows,
+                     offsets, w.poff, (int)E, static_cast<T*>(w.x_t), np);
+  hipLaunchKernelGGL((pad_transpose_kernel<T>), gd, dim3(256), 0, s, static_cast<const T*>(dy_perm), d, 0,
+                     (const int32_t*)nullptr, offsets, w.poff, (int)E, static_cast<T*>(w.dy_t), np);
+  hipLaunchKernelGGL((pad_transpose_kernel<T>), gf, dim3(256), 0, s, static_cast<const T*>(w.h), F, 0,
+                     (const int32_t*)nullptr, offsets, w.poff, (int)E, static_cast<T*>(w.h_t), np);
+  hipLaunchKernelGGL((pad_transpose_kernel<T>), gf, dim3(256), 0, s, static_cast<const T*>(w.dgu), 2 * F, 0,
+                     (const int32_t*)nullptr, offsets, w.poff, (int)E, static_cast<T*>(w.dg_t), np);
+  hipLaunchKernelGGL((pad_transpose_kernel<T>), gf, dim3(256), 0, s, static_cast<const T*>(w.dgu), 2 * F, (int)F,
+                     (const int32_t*)nullptr, offsets, w.poff, (int)E, static_cast<T*>(w.du_t), np);
+
+  // weight gradients: one group per expert, k over its padded column range
+  auto wgrad = [&](const void* A, int rows, const void* B, int N, float* C) {
+    GemmArgs a = args_grouped(A, nullptr, B, nullptr, 0, nullptr, (int)E, E * rows, N, 0, C);
+    a.group_rows = rows;
+    a.a_shared = 1;
+    a.lda = np;
+    a.ldb = np;
+    a.kseg = w.poff;
+    gemm<T, BK, EPI_F32_BIAS>(a, num_cu, s);
+  };
+  wgrad(w.dy_t, (int)d, w.h_t, (int)F, dw_down);
+  wgrad(w.dg_t, (int)F, w.x_t, (int)d, dw_gate);
+  wgrad(w.du_t, (int)F, w.x_t, (int)d, dw_up);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -25,7 +25,9 @@
 
 namespace moe {
 
-enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2, EPI_AXPBY = 3 };
+enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2, EPI_AXPBY = 3, EPI_SWIGLU_BWD = 4 };
+// Epilogues whose B tile holds gate rows and the matching up rows.
+constexpr bool paired_epilogue(int epi) { return epi == EPI_SWIGLU || epi == EPI_SWIGLU_BWD; }
 
 // f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
 template <int N, int I = 0, typename F> __device__ __forceinline__ void static_for(F&& f) {
@@ -66,6 +68,14 @@ struct GemmArgs {
   int32_t m_chunk;        // tile order: row tiles per chunk (<= 0: all row tiles of a group)
   float alpha, beta;      // EPI_AXPBY: C = alpha * (A B^T) + beta * D
   const void* D;          // EPI_AXPBY: [rows, N], same layout and type as C
+                          // EPI_SWIGLU_BWD: dH [rows, N] float32
+  int64_t lda, ldb;       // row strides of A and B in elements (0: K)
+  const int32_t* kseg;    // [G+1] device k offsets (multiples of BK): group g contracts
+                          // over k in [kseg[g], kseg[g+1]) (nullptr: [0, K) for all)
+  int32_t a_shared;       // 1: every group reads the same A rows (row r of a group's
+                          // tile block is A row r, not the group's first row + r)
+  void* C2;               // EPI_SWIGLU_BWD: H = silu(G) * U, [rows, N]
+  int64_t ldc;            // row stride of C in elements (0: N)
 };
 
 // Per element type: how one wave multiplies a 32x32 block over 16 k values.
@@ -179,14 +189,14 @@ struct GemmTile {
   static constexpr int MI = WTM / 32, NI = WTN / 32;
   static constexpr int kSub = BK / 16;                // 16-k MFMA sub-steps per k-tile
   static constexpr int CPL = 8 * (int)sizeof(T) / 16; // chunks per lane per fragment
-  static constexpr int NOUT = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+  static constexpr int NOUT = paired_epilogue(EPI) ? BN / 2 : BN;
   static constexpr int kLdsBytes = STAGES * kStageBytes;
 
   static_assert(RB == 64 || RB == 128, "LDS row must be 64 or 128 bytes");
   static_assert(kChunks % kThreads == 0, "stage must split evenly over threads");
   static_assert(BM % kRowsPerStep == 0 && BN % kRowsPerStep == 0, "load steps must not straddle A and B");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be made of 32x32 blocks");
-  static_assert(EPI != EPI_SWIGLU || (NI % 2 == 0 && (BN / 2) % kRowsPerStep == 0), "SwiGLU needs paired blocks");
+  static_assert(!paired_epilogue(EPI) || (NI % 2 == 0 && (BN / 2) % kRowsPerStep == 0), "SwiGLU needs paired blocks");
   static_assert(STAGES >= 2, "need at least double buffering");
 
   // gfx950 serves a ds_read_b128 16 lanes at a time across 64 four-byte banks (a
@@ -197,7 +207,7 @@ struct GemmTile {
 
   // LDS row (within the B region) that MFMA column block ni of wave column wn reads.
   __device__ __forceinline__ static int b_row(int wn, int ni) {
-    if (EPI == EPI_SWIGLU) {
+    if (paired_epilogue(EPI)) {
       constexpr int H = NI / 2;
       return ni < H ? wn * (WTN / 2) + ni * 32 : BN / 2 + wn * (WTN / 2) + (ni - H) * 32;
     }
@@ -267,13 +277,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   if (!uniform) build_tile_prefix<BM, NT>(p.seg, G, p.M, p.group_rows, ntn, tstart);
   const int total = uniform ? G * per_g : __builtin_amdgcn_readfirstlane(tstart[G]);
   const int K = p.K;
-  const int nk = K / BK;
+  const int64_t lda = p.lda ? p.lda : K, ldb = p.ldb ? p.ldb : K;
   const T* __restrict__ Abase = static_cast<const T*>(p.A);
 
   // ---- tile bookkeeping (all wave-uniform) ------------------------------------
   struct TileInfo {
-    int g, n0, rows_valid;
-    int64_t m0;
+    int g, n0, rows_valid, nk;
+    int64_t m0, mrel, k0;   // first output row, its offset in the group, first k
   };
   auto locate = [&](int tile) -> TileInfo {
     TileInfo t;
@@ -309,8 +319,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     const int sz = min(NG, ntn - cg * NG);
     const int mt = base_m + l2 / sz, nt = cg * NG + l2 % sz;
     t.m0 = seg_lo + (int64_t)mt * BM;
+    t.mrel = (int64_t)mt * BM;
     t.n0 = nt * NOUT;
     t.rows_valid = (int)min<int64_t>(BM, seg_hi - t.m0);
+    t.k0 = p.kseg ? (int64_t)p.kseg[t.g] : 0;
+    t.nk = p.kseg ? (int)(((int64_t)p.kseg[t.g + 1] - t.k0) / BK) : K / BK;
     return t;
   };
 
@@ -334,11 +347,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   const char* Bub = nullptr;
   uint32_t soff[CPT];
   auto setup = [&](const TileInfo& t, const int* arow) {
-    Ab = reinterpret_cast<const char*>(p.a_rows ? Abase : Abase + t.m0 * K);
-    Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)t.g * p.b_stride + (int64_t)t.n0 * K);
-    if (EPI == EPI_SWIGLU)
+    Ab = reinterpret_cast<const char*>(Abase + t.k0 + (p.a_rows ? 0 : (p.a_shared ? t.mrel : t.m0) * lda));
+    Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)t.g * p.b_stride + (int64_t)t.n0 * ldb +
+                                        t.k0);
+    if (paired_epilogue(EPI))
       Bub = reinterpret_cast<const char*>(static_cast<const T*>(p.B1) + (int64_t)t.g * p.b_stride +
-                                          (int64_t)t.n0 * K);
+                                          (int64_t)t.n0 * ldb + t.k0);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       // whether load step i reads A, gate or up is known at compile time
@@ -350,11 +364,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
         r = arow[i];
       } else {
         const int br = row - BM;
-        const int half = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+        const int half = paired_epilogue(EPI) ? BN / 2 : BN;
         const int n = (br < half) ? br : br - half;
         r = min(n, p.N - t.n0 - 1);                            // columns past N: any valid column
       }
-      soff[i] = ((uint32_t)r * (uint32_t)K + (uint32_t)(lc * EPC)) * (uint32_t)sizeof(T);
+      soff[i] = ((uint32_t)r * (uint32_t)(i < CPA ? lda : ldb) + (uint32_t)(lc * EPC)) * (uint32_t)sizeof(T);
     }
   };
   // copy i (of CPT) of k-tile kt into `stage`
@@ -364,7 +378,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     const int row0 = i * Cfg::kRowsPerStep;
     const char* base;
     if (row0 < BM) base = Ab;
-    else if (EPI == EPI_SWIGLU && row0 - BM >= BN / 2) base = Bub;
+    else if (paired_epilogue(EPI) && row0 - BM >= BN / 2) base = Bub;
     else base = Bgb;
     lds_dma16(base + kb, soff[i], lbase + i * NT * 16);
   };
@@ -372,10 +386,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
 #pragma unroll
     for (int i = 0; i < CPT; ++i) load_one(stage, kt, i);
   };
-  auto prologue = [&]() {
+  auto prologue = [&](int nkt) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
-      if (s < nk) load_stage(s, s);
+      if (s < nkt) load_stage(s, s);
   };
 
   // Row blocks past the end of a ragged row tile carry no output: their MFMAs and
@@ -471,15 +485,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
             }
           }
       }
-    } else if constexpr (EPI != EPI_AXPBY && NT == 512 && Cfg::WTM == 64 && 8 * kEpiWaveBytes <= Cfg::kStageBytes) {
+    } else if constexpr (EPI != EPI_AXPBY && EPI != EPI_SWIGLU_BWD && NT == 512 && Cfg::WTM == 64 &&
+                         8 * kEpiWaveBytes <= Cfg::kStageBytes) {
       // Staged through LDS (wbuf: this wave's 32 rows x 144 bytes, which nothing
       // else touches until the next barrier).  Per round
       // (one row block mi, 128 bytes of output columns) it parks its values there
       // (the 16-byte pad spreads rows over the banks and keeps every address a lane
       // base plus an immediate), then reads them back as 16-byte pieces, 8 lanes per
       // row, and stores whole 128-byte row segments.
-      constexpr int NO = (EPI == EPI_SWIGLU) ? NI / 2 : NI;
-      constexpr int CW = (EPI == EPI_SWIGLU) ? Cfg::WTN / 2 : Cfg::WTN;   // output columns per wave
+      constexpr int NO = paired_epilogue(EPI) ? NI / 2 : NI;
+      constexpr int CW = paired_epilogue(EPI) ? Cfg::WTN / 2 : Cfg::WTN;   // output columns per wave
       constexpr int ES = (int)sizeof(T);
       constexpr int RC = 128 / ES;                                         // columns per round
       constexpr int ROUNDS = CW / RC;
@@ -529,19 +544,41 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
         }
       }
     } else {
-      constexpr int NO = (EPI == EPI_SWIGLU) ? NI / 2 : NI;
-      constexpr int CW = (EPI == EPI_SWIGLU) ? Cfg::WTN / 2 : Cfg::WTN;
+      constexpr int NO = paired_epilogue(EPI) ? NI / 2 : NI;
+      constexpr int CW = paired_epilogue(EPI) ? Cfg::WTN / 2 : Cfg::WTN;
+      const int64_t ldc = p.ldc ? p.ldc : p.N;
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         const int r = wm * Cfg::WTM + mi * 32 + (lane & 31);
         if (r >= erows) continue;
-        T* crow = static_cast<T*>(p.C) + (em0 + r) * (int64_t)p.N;
+        T* crow = static_cast<T*>(p.C) + (em0 + r) * ldc;
 #pragma unroll
         for (int ni = 0; ni < NO; ++ni)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int col = en0 + wn * CW + ni * 32 + 8 * q + h4;
-            if (col < p.N) {
+            if constexpr (EPI == EPI_SWIGLU_BWD) {
+              // recomputed G and U with the incoming dH:  S = silu(G), H = S U,
+              // dU = dH S, dG = dH U silu'(G); dG and dU go to the row's two halves
+              if (col < p.N) {
+                const f32x4 dh =
+                    *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.D) + (em0 + r) * (int64_t)p.N + col);
+                float dg[4], du[4], hh[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const float g = acc[mi][ni][4 * q + i];
+                  const float u = acc[mi][ni + NI / 2][4 * q + i];
+                  const float sg = 1.0f / (1.0f + __expf(-g));
+                  const float sv = g * sg;
+                  du[i] = dh[i] * sv;
+                  dg[i] = dh[i] * u * (sg * (1.0f + g * (1.0f - sg)));
+                  hh[i] = sv * u;
+                }
+                store4(crow + col, dg);
+                store4(crow + p.N + col, du);
+                store4(static_cast<T*>(p.C2) + (em0 + r) * (int64_t)p.N + col, hh);
+              }
+            } else if (col < p.N) {
               float v[4];
               float dv[4] = {0.f, 0.f, 0.f, 0.f};
               if constexpr (EPI == EPI_AXPBY)
@@ -579,9 +616,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   int arow[CPA], arow_n[CPA];
   fetch_rows(cur, arow);
   setup(cur, arow);
-  prologue();
+  prologue(cur.nk);
 
   while (true) {
+    const int nk = cur.nk;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -659,7 +697,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     block_barrier();
     if (more) {
       setup(nxt, arow_n);
-      prologue();
+      prologue(nxt.nk);
     }
     store_tile(cur, smem + (STAGES - 1) * Cfg::kStageBytes + wave * kEpiWaveBytes);
     if (!more) break;

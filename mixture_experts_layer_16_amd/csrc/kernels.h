@@ -40,6 +40,28 @@ hipError_t launch_newton_schulz(int64_t n, int64_t R, int64_t C, int64_t steps, 
                                 float eps, const void* g, void* x, void* xw, void* xt0, void* xt1, void* A,
                                 void* B, float* partial, int num_cu, hipStream_t stream);
 
+// Backward of the grouped SwiGLU FFN (bf16): dx_perm and the float32 weight
+// gradients from dy_perm.  Scratch (caller-carved):
+struct FfnBackwardScratch {
+  int32_t* poff;   // [E+1] padded expert column offsets
+  void* wd_t;      // [E, F, d]   W_d transposed
+  void* wgu_t;     // [E, d, 2F]  W_g and W_u transposed, side by side
+  float* dh;       // [n_max, F]  dH (float32)
+  void* dgu;       // [n_max, 2F] dG | dU
+  void* h;         // [n_max, F]  H recomputed
+  void* x_t;       // [d, n_pad]  expert rows of the input, transposed and padded
+  void* dy_t;      // [d, n_pad]
+  void* h_t;       // [F, n_pad]
+  void* dg_t;      // [F, n_pad]
+  void* du_t;      // [F, n_pad]
+  int64_t n_pad;   // >= sum over experts of rows rounded up to 64; a multiple of 64
+};
+hipError_t launch_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_in,
+                                       const int32_t* a_rows, const int32_t* offsets, const void* w_gate,
+                                       const void* w_up, const void* w_down, const void* dy_perm, void* dx_perm,
+                                       float* dw_gate, float* dw_up, float* dw_down, const FfnBackwardScratch& w,
+                                       int num_cu, hipStream_t stream);
+
 // Weighted un-permute: y[t] = sum_j w[t,j] * y_perm[slot_row[t,j]].
 hipError_t launch_combine(int dtype, int64_t T, int64_t d, int64_t k, const void* y_perm,
                           const int32_t* slot_row, const float* w, void* y, hipStream_t stream);

@@ -178,6 +178,55 @@ moe_status moe_grouped_ffn(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_d
                                             y_perm, ws, ncu, static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_dtype dtype,
+                                    const void* x_in, int64_t n_in, const int32_t* a_rows, const int32_t* offsets,
+                                    const void* w_gate, const void* w_up, const void* w_down, const void* dy_perm,
+                                    void* dx_perm, float* dw_gate, float* dw_up, float* dw_down, void* ws,
+                                    size_t* ws_bytes, void* stream) {
+  moe_status st = check_ffn_dims(n_max, d, E, F);
+  if (st != MOE_OK) return st;
+  if (dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (a_rows != nullptr) {
+    if (n_in <= 0) return MOE_ERR_INVALID_ARG;
+    if ((uint64_t)n_in * (uint64_t)d * 2 >= (uint64_t(1) << 32)) return MOE_ERR_UNSUPPORTED;
+  }
+  const int64_t n_pad = (n_max + 63 * E + 63) / 64 * 64;
+  if (n_pad >= kIdxLimit) return MOE_ERR_UNSUPPORTED;
+  auto carve = [&](Carver& c, moe::FfnBackwardScratch& w) {
+    w.poff = static_cast<int32_t*>(c.take((size_t)(E + 1) * 4));
+    w.wd_t = c.take((size_t)E * F * d * 2);
+    w.wgu_t = c.take((size_t)E * d * 2 * F * 2);
+    w.dh = static_cast<float*>(c.take((size_t)n_max * F * 4));
+    w.dgu = c.take((size_t)n_max * 2 * F * 2);
+    w.h = c.take((size_t)n_max * F * 2);
+    w.x_t = c.take((size_t)d * n_pad * 2);
+    w.dy_t = c.take((size_t)d * n_pad * 2);
+    w.h_t = c.take((size_t)F * n_pad * 2);
+    w.dg_t = c.take((size_t)F * n_pad * 2);
+    w.du_t = c.take((size_t)F * n_pad * 2);
+    w.n_pad = n_pad;
+  };
+  moe::FfnBackwardScratch w{};
+  Carver c0(nullptr);
+  carve(c0, w);
+  const size_t need = c0.used;
+  if (ws == nullptr && ws_bytes != nullptr) {
+    *ws_bytes = need;
+    return MOE_OK;
+  }
+  if (!ok16(x_in) || !opt4(a_rows) || !ok4(offsets) || !ok16(w_gate) || !ok16(w_up) || !ok16(w_down) ||
+      !ok16(dy_perm) || !ok16(dx_perm) || !ok16(dw_gate) || !ok16(dw_up) || !ok16(dw_down))
+    return MOE_ERR_INVALID_ARG;
+  if (workspace_step(ws, ws_bytes, need, &st)) return st;
+  int ncu = 0;
+  if ((st = num_cu(&ncu)) != MOE_OK) return st;
+  Carver cv(ws);
+  carve(cv, w);
+  return hip_status(moe::launch_grouped_ffn_backward(n_max, d, E, F, x_in, a_rows, offsets, w_gate, w_up, w_down,
+                                                     dy_perm, dx_perm, dw_gate, dw_up, dw_down, w, ncu,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_newton_schulz(int64_t n, int64_t R, int64_t C, moe_dtype dtype, int64_t steps, float a, float b,
                              float c, float eps, const void* g, void* x, void* ws, size_t* ws_bytes, void* stream) {
   if (n <= 0 || R <= 0 || C <= 0 || steps < 0 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;

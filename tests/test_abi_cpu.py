@@ -217,3 +217,38 @@ def test_newton_schulz_workspace_query(n, R, C):
 ])
 def test_newton_schulz_argument_errors(kw, status):
     assert ns(**kw) == status
+
+
+# ---- expert-FFN backward --------------------------------------------------------
+
+def bwd_ws(n_max, d, E, F):
+    n_pad = (n_max + 63 * E + 63) // 64 * 64
+    return (ru((E + 1) * 4) + ru(E * F * d * 2) + ru(E * d * 2 * F * 2) + ru(n_max * F * 4) + ru(n_max * 2 * F * 2)
+            + ru(n_max * F * 2) + 2 * ru(d * n_pad * 2) + 3 * ru(F * n_pad * 2))
+
+
+@pytest.mark.parametrize("n_max,d,E,F", [(1000, 128, 4, 192), (524288, 6144, 384, 1792), (64, 64, 1, 64)])
+def test_ffn_backward_workspace_query(n_max, d, E, F):
+    nb = ctypes.c_size_t(12345)
+    st = B.lib().moe_grouped_ffn_backward(n_max, d, E, F, 1, P, 0, None, P, P, P, P, P, P, P, P, P, None,
+                                          ctypes.byref(nb), None)
+    assert st == OK and nb.value == bwd_ws(n_max, d, E, F)
+
+
+def bwd(n_max=1000, d=128, E=4, F=128, dt=1, xp=P, n_in=0, rows=None, off=P, wg=P, wu=P, wd=P, dy=P, dx=P,
+        dwg=P, dwu=P, dwd=P, ws=P, nbytes=1 << 36):
+    nb = ctypes.c_size_t(nbytes)
+    return B.lib().moe_grouped_ffn_backward(n_max, d, E, F, dt, xp, n_in, rows, off, wg, wu, wd, dy, dx, dwg,
+                                            dwu, dwd, ws, ctypes.byref(nb), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_max=0), INVALID), (dict(F=0), INVALID), (dict(F=100), UNSUPPORTED), (dict(d=65), UNSUPPORTED),
+    (dict(E=2000), UNSUPPORTED), (dict(dt=0), UNSUPPORTED), (dict(dt=9), UNSUPPORTED),
+    (dict(xp=None), INVALID), (dict(off=None), INVALID), (dict(dy=P_MIS), INVALID), (dict(dx=None), INVALID),
+    (dict(dwg=P_MIS), INVALID), (dict(dwd=None), INVALID), (dict(nbytes=1000), WORKSPACE),
+    (dict(rows=P, n_in=0), INVALID), (dict(rows=P, n_in=(1 << 31) // 128), UNSUPPORTED),
+    (dict(rows=ctypes.c_void_p(0x10001), n_in=100), INVALID),
+])
+def test_ffn_backward_argument_errors(kw, status):
+    assert bwd(**kw) == status
