@@ -12,6 +12,9 @@ the bf16 dense MFMA peak; `stages_ms` gives each step's average duration from
 a second, stage-by-stage pass; `cpu_baseline` times the float64 CPU oracle on a
 bounded slice of the same workload.
 
+`--path backward` measures the grouped expert-FFN backward (dX and the three
+weight gradients from dY) on the routing of the same workload.
+
 `--path newton_schulz` measures the next row instead: Muon's Newton-Schulz
 orthogonalisation of whole expert matrices (one step = the gate, up and down
 matrices of the 96 experts one expert-parallel rank owns, five quintic steps
@@ -40,9 +43,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="page_seq64k_skewed")
-    ap.add_argument("--path", default="layer", choices=["layer", "newton_schulz"],
+    ap.add_argument("--path", default="layer", choices=["layer", "newton_schulz", "backward"],
                     help="layer: the MoE layer forward (default); newton_schulz: Muon's orthogonalisation "
-                         "of whole expert matrices")
+                         "of whole expert matrices; backward: the grouped expert-FFN backward")
     ap.add_argument("--ns-experts", type=int, default=96,
                     help="newton_schulz: experts whose gate, up and down matrices one step orthogonalises")
     ap.add_argument("--cpu-tokens", type=int, default=512,
@@ -216,6 +219,76 @@ def bench_newton_schulz(args, torch, B):
     print(json.dumps(out), flush=True)
 
 
+BWD_METRIC = "MoE expert-FFN backward tokens/s + % bf16 MFMA peak (d6144,E384,top8)"
+
+
+def bench_backward(args, torch, B, W):
+    """One step: moe_grouped_ffn_backward over every slot of the workload (token
+    rows read in place), dY random.  Algorithmic work 12 N d F (dH, dX, three
+    weight gradients); the kernels also recompute G and U (4 N d F more)."""
+    import numpy as np
+    wl = W.WORKLOADS[args.workload]
+    inp = W.make_inputs(wl, device="cuda:0")
+    if inp["w_router"] is not None:
+        ids, w, _ = B.moe_route(inp["x"], inp["w_router"], wl.k, bias=inp["bias"], want_logits=False)
+    else:
+        ids, w = inp["topk_ids"], inp["topk_w"]
+    off, rt, sr, _ = B.moe_permute(inp["x"], ids, wl.E, copy_rows=False)
+    g = torch.Generator(device="cuda:0").manual_seed(1)
+    dy = torch.randn(rt.numel(), wl.d, generator=g, device="cuda:0").to(wl.dtype)
+    call = B.GroupedFfnBackward(inp["x"], off, inp["w_gate"], inp["w_up"], inp["w_down"], dy, a_rows=rt)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        call()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    n = int(off[-1])
+    flops = 12 * n * wl.d * wl.F
+    tflops = flops / (ms / 1e3) / 1e12
+    out = {
+        "metric": BWD_METRIC, "value": round(wl.T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random inputs, weights and output gradients of the page's layer shape)",
+        "config": {"workload": wl.name + "_backward", "tokens": wl.T, "hidden": wl.d, "experts": wl.E,
+                   "top_k": wl.k, "expert_hidden": wl.F, "slots": n},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "moe_grouped_ffn_backward (7 GEMM launches, weight and activation transposes)",
+                     "flops_per_launch": flops, "ms_per_launch": round(ms, 4),
+                     "note": "achieved counts 12 N d F; the G/U recompute (4 N d F) is extra work"},
+    }
+    if args.cpu_tokens > 0:
+        from threadpoolctl import threadpool_info
+        from oracle import moe_backward_oracle as bo
+        from oracle import moe_oracle as orc
+        nt = min(args.cpu_tokens, wl.T)
+        ids_h = ids[:nt].cpu().numpy().astype(np.int64)
+        off_h, rt_h, _ = orc.permute(ids_h, wl.E)
+        X = inp["x"][:nt].float().cpu().numpy().astype(np.float64)[rt_h]
+        dY = np.random.default_rng(2).standard_normal((len(rt_h), wl.d))
+        f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+        used = [e for e in range(wl.E) if off_h[e + 1] > off_h[e]]
+        wg = {e: f64(inp["w_gate"][e]) for e in used}
+        wu = {e: f64(inp["w_up"][e]) for e in used}
+        wd = {e: f64(inp["w_down"][e]) for e in used}
+        t0 = time.perf_counter()
+        for e in used:
+            lo, hi = off_h[e], off_h[e + 1]
+            bo.expert_ffn_backward(X[lo:hi], wg[e], wu[e], wd[e], dY[lo:hi])
+        dt = time.perf_counter() - t0
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        out["cpu_baseline"] = {"value": round(nt / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"first {nt} of {wl.T} tokens ({len(rt_h)} slots, {len(used)} experts): "
+                                         f"float64 expert backward {dt:.1f} s on {threads} BLAS threads"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -231,6 +304,9 @@ def main():
     torch.cuda.set_device(0)
     if args.path == "newton_schulz":
         bench_newton_schulz(args, torch, B)
+        return
+    if args.path == "backward":
+        bench_backward(args, torch, B, W)
         return
     wl = W.WORKLOADS[args.workload]
     if args.traffic_probe:

@@ -246,7 +246,10 @@ __device__ void build_tile_prefix(const int32_t* seg, int G, int64_t M, int64_t 
 }
 
 // PD: how many 16-k sub-steps ahead the MFMA operand fragments are read from LDS
-template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, int PD = 1>
+// GEN: honour lda, ldb, kseg, a_shared and equal groups without offsets
+// (group_rows); otherwise those are ignored, the operands are [rows, K] with one
+// K for every group, and the groups come from seg (or are one group of M rows).
+template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, int PD = 1, bool GEN = false>
 __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs p) {
   typedef GemmTile<T, BM, BN, BK, WM, WN, STAGES, EPI> Cfg;
   typedef Mma<T> Op;
@@ -269,15 +272,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  const int G = (p.seg || p.group_rows > 0) ? p.G : 1;
+  const int G = (p.seg || (GEN && p.group_rows > 0)) ? p.G : 1;
   const int ntn = (p.N + NOUT - 1) / NOUT;
   // equal groups (a batch of matrices): group g owns tiles [g * per_g, (g+1) * per_g)
-  const bool uniform = p.seg == nullptr;
+  const bool uniform = GEN && p.seg == nullptr;
   const int per_g = uniform ? (int)((p.group_rows > 0 ? p.group_rows : p.M) + BM - 1) / BM * ntn : 0;
-  if (!uniform) build_tile_prefix<BM, NT>(p.seg, G, p.M, p.group_rows, ntn, tstart);
+  if (!uniform) build_tile_prefix<BM, NT>(p.seg, G, p.M, GEN ? p.group_rows : 0, ntn, tstart);
   const int total = uniform ? G * per_g : __builtin_amdgcn_readfirstlane(tstart[G]);
   const int K = p.K;
-  const int64_t lda = p.lda ? p.lda : K, ldb = p.ldb ? p.ldb : K;
+  const int64_t lda = (GEN && p.lda) ? p.lda : K, ldb = (GEN && p.ldb) ? p.ldb : K;
   const T* __restrict__ Abase = static_cast<const T*>(p.A);
 
   // ---- tile bookkeeping (all wave-uniform) ------------------------------------
@@ -300,8 +303,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
       t.g = __builtin_amdgcn_readfirstlane(lo);
       local = tile - __builtin_amdgcn_readfirstlane(tstart[t.g]);
     }
-    const int64_t seg_lo = p.seg ? (int64_t)p.seg[t.g] : (int64_t)t.g * p.group_rows;
-    const int64_t seg_hi = p.seg ? (int64_t)p.seg[t.g + 1] : (p.group_rows > 0 ? seg_lo + p.group_rows : p.M);
+    const int64_t grows = GEN ? p.group_rows : 0;
+    const int64_t seg_lo = p.seg ? (int64_t)p.seg[t.g] : (int64_t)t.g * grows;
+    const int64_t seg_hi = p.seg ? (int64_t)p.seg[t.g + 1] : (grows > 0 ? seg_lo + grows : p.M);
     // Within a group the tiles run in chunks of SM row tiles; inside a chunk, in
     // column groups of NG column tiles; inside a column group, row tile by row
     // tile.  Consecutive tiles then share A rows (same row tile) and B columns
@@ -322,8 +326,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     t.mrel = (int64_t)mt * BM;
     t.n0 = nt * NOUT;
     t.rows_valid = (int)min<int64_t>(BM, seg_hi - t.m0);
-    t.k0 = p.kseg ? (int64_t)p.kseg[t.g] : 0;
-    t.nk = p.kseg ? (int)(((int64_t)p.kseg[t.g + 1] - t.k0) / BK) : K / BK;
+    t.k0 = (GEN && p.kseg) ? (int64_t)p.kseg[t.g] : 0;
+    t.nk = (GEN && p.kseg) ? (int)(((int64_t)p.kseg[t.g + 1] - t.k0) / BK) : K / BK;
     return t;
   };
 
@@ -347,12 +351,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   const char* Bub = nullptr;
   uint32_t soff[CPT];
   auto setup = [&](const TileInfo& t, const int* arow) {
-    Ab = reinterpret_cast<const char*>(Abase + t.k0 + (p.a_rows ? 0 : (p.a_shared ? t.mrel : t.m0) * lda));
+    const int64_t k0 = GEN ? t.k0 : 0;
+    Ab = reinterpret_cast<const char*>(Abase + k0 + (p.a_rows ? 0 : ((GEN && p.a_shared) ? t.mrel : t.m0) * lda));
     Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)t.g * p.b_stride + (int64_t)t.n0 * ldb +
-                                        t.k0);
+                                        k0);
     if (paired_epilogue(EPI))
       Bub = reinterpret_cast<const char*>(static_cast<const T*>(p.B1) + (int64_t)t.g * p.b_stride +
-                                          (int64_t)t.n0 * ldb + t.k0);
+                                          (int64_t)t.n0 * ldb + k0);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       // whether load step i reads A, gate or up is known at compile time
@@ -546,7 +551,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     } else {
       constexpr int NO = paired_epilogue(EPI) ? NI / 2 : NI;
       constexpr int CW = paired_epilogue(EPI) ? Cfg::WTN / 2 : Cfg::WTN;
-      const int64_t ldc = p.ldc ? p.ldc : p.N;
+      const int64_t ldc = (EPI == EPI_SWIGLU_BWD && p.ldc) ? p.ldc : p.N;
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         const int r = wm * Cfg::WTM + mi * 32 + (lane & 31);
@@ -616,10 +621,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   int arow[CPA], arow_n[CPA];
   fetch_rows(cur, arow);
   setup(cur, arow);
-  prologue(cur.nk);
+  prologue(GEN ? cur.nk : K / BK);
 
   while (true) {
-    const int nk = cur.nk;
+    const int nk = GEN ? cur.nk : K / BK;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -697,7 +702,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     block_barrier();
     if (more) {
       setup(nxt, arow_n);
-      prologue(nxt.nk);
+      prologue(GEN ? nxt.nk : K / BK);
     }
     store_tile(cur, smem + (STAGES - 1) * Cfg::kStageBytes + wave * kEpiWaveBytes);
     if (!more) break;
