@@ -122,9 +122,9 @@ GemmArgs args_grouped(const void* A, const int32_t* a_rows, const void* B0, cons
   return a;
 }
 
-template <typename T, int BK, int EPI, bool GEN = false>
+template <typename T, int BK, int EPI, int FEAT = 0>
 void gemm(const GemmArgs& a, int num_cu, hipStream_t s) {
-  hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, 4, 2, 2, EPI, 1, GEN>), dim3(num_cu), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, 4, 2, 2, EPI, 1, FEAT>), dim3(num_cu), dim3(512), 0, s, a);
 }
 
 }  // namespace
@@ -186,7 +186,7 @@ hipError_t launch_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int6
     a.lda = np;
     a.ldb = np;
     a.kseg = w.poff;
-    gemm<T, BK, EPI_F32_BIAS, true>(a, num_cu, s);
+    gemm<T, BK, EPI_F32_BIAS, kFeatGroups | kFeatStrides>(a, num_cu, s);
   };
   wgrad(w.dy_t, (int)d, w.h_t, (int)F, dw_down);
   wgrad(w.dg_t, (int)F, w.x_t, (int)d, dw_gate);

@@ -25,6 +25,8 @@
 
 namespace moe {
 
+enum GemmFeature { kFeatGroups = 1, kFeatStrides = 2 };
+
 enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2, EPI_AXPBY = 3, EPI_SWIGLU_BWD = 4 };
 // Epilogues whose B tile holds gate rows and the matching up rows.
 constexpr bool paired_epilogue(int epi) { return epi == EPI_SWIGLU || epi == EPI_SWIGLU_BWD; }
@@ -246,10 +248,12 @@ __device__ void build_tile_prefix(const int32_t* seg, int G, int64_t M, int64_t 
 }
 
 // PD: how many 16-k sub-steps ahead the MFMA operand fragments are read from LDS
-// GEN: honour lda, ldb, kseg, a_shared and equal groups without offsets
-// (group_rows); otherwise those are ignored, the operands are [rows, K] with one
-// K for every group, and the groups come from seg (or are one group of M rows).
-template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, int PD = 1, bool GEN = false>
+// FEAT (compile-time, so that kernels without them compile as if absent):
+//   kFeatGroups:  equal groups without offsets (seg == nullptr, group_rows > 0);
+//   kFeatStrides: lda, ldb, kseg and a_shared;
+// otherwise those fields are ignored: operands are [rows, K] with one K for every
+// group, and the groups come from seg (or are one group of M rows).
+template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, int PD = 1, int FEAT = 0>
 __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs p) {
   typedef GemmTile<T, BM, BN, BK, WM, WN, STAGES, EPI> Cfg;
   typedef Mma<T> Op;
@@ -261,6 +265,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
   constexpr int KSUB = Cfg::kSub;
   static_assert(PD >= 1 && PD < KSUB, "prefetch distance must be 1 .. sub-steps - 1");
+  constexpr bool GRP = (FEAT & kFeatGroups) != 0, STR = (FEAT & kFeatStrides) != 0;
 
   constexpr int kEpiRowBytes = 144;                 // staging row stride of the epilogue (bytes)
   constexpr int kEpiWaveBytes = 32 * kEpiRowBytes;  // one wave's staging buffer: 32 rows
@@ -272,15 +277,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
-  const int G = (p.seg || (GEN && p.group_rows > 0)) ? p.G : 1;
+  const int G = (p.seg || (GRP && p.group_rows > 0)) ? p.G : 1;
   const int ntn = (p.N + NOUT - 1) / NOUT;
   // equal groups (a batch of matrices): group g owns tiles [g * per_g, (g+1) * per_g)
-  const bool uniform = GEN && p.seg == nullptr;
+  const bool uniform = GRP && p.seg == nullptr;
   const int per_g = uniform ? (int)((p.group_rows > 0 ? p.group_rows : p.M) + BM - 1) / BM * ntn : 0;
-  if (!uniform) build_tile_prefix<BM, NT>(p.seg, G, p.M, GEN ? p.group_rows : 0, ntn, tstart);
+  if (!uniform) build_tile_prefix<BM, NT>(p.seg, G, p.M, GRP ? p.group_rows : 0, ntn, tstart);
   const int total = uniform ? G * per_g : __builtin_amdgcn_readfirstlane(tstart[G]);
   const int K = p.K;
-  const int64_t lda = (GEN && p.lda) ? p.lda : K, ldb = (GEN && p.ldb) ? p.ldb : K;
+  const int64_t lda = (STR && p.lda) ? p.lda : K, ldb = (STR && p.ldb) ? p.ldb : K;
   const T* __restrict__ Abase = static_cast<const T*>(p.A);
 
   // ---- tile bookkeeping (all wave-uniform) ------------------------------------
@@ -303,7 +308,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
       t.g = __builtin_amdgcn_readfirstlane(lo);
       local = tile - __builtin_amdgcn_readfirstlane(tstart[t.g]);
     }
-    const int64_t grows = GEN ? p.group_rows : 0;
+    const int64_t grows = GRP ? p.group_rows : 0;
     const int64_t seg_lo = p.seg ? (int64_t)p.seg[t.g] : (int64_t)t.g * grows;
     const int64_t seg_hi = p.seg ? (int64_t)p.seg[t.g + 1] : (grows > 0 ? seg_lo + grows : p.M);
     // Within a group the tiles run in chunks of SM row tiles; inside a chunk, in
@@ -326,8 +331,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     t.mrel = (int64_t)mt * BM;
     t.n0 = nt * NOUT;
     t.rows_valid = (int)min<int64_t>(BM, seg_hi - t.m0);
-    t.k0 = (GEN && p.kseg) ? (int64_t)p.kseg[t.g] : 0;
-    t.nk = (GEN && p.kseg) ? (int)(((int64_t)p.kseg[t.g + 1] - t.k0) / BK) : K / BK;
+    t.k0 = (STR && p.kseg) ? (int64_t)p.kseg[t.g] : 0;
+    t.nk = (STR && p.kseg) ? (int)(((int64_t)p.kseg[t.g + 1] - t.k0) / BK) : K / BK;
     return t;
   };
 
@@ -351,8 +356,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   const char* Bub = nullptr;
   uint32_t soff[CPT];
   auto setup = [&](const TileInfo& t, const int* arow) {
-    const int64_t k0 = GEN ? t.k0 : 0;
-    Ab = reinterpret_cast<const char*>(Abase + k0 + (p.a_rows ? 0 : ((GEN && p.a_shared) ? t.mrel : t.m0) * lda));
+    const int64_t k0 = STR ? t.k0 : 0;
+    Ab = reinterpret_cast<const char*>(Abase + k0 + (p.a_rows ? 0 : ((STR && p.a_shared) ? t.mrel : t.m0) * lda));
     Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)t.g * p.b_stride + (int64_t)t.n0 * ldb +
                                         k0);
     if (paired_epilogue(EPI))
@@ -621,10 +626,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   int arow[CPA], arow_n[CPA];
   fetch_rows(cur, arow);
   setup(cur, arow);
-  prologue(GEN ? cur.nk : K / BK);
+  prologue(STR ? cur.nk : K / BK);
 
   while (true) {
-    const int nk = GEN ? cur.nk : K / BK;
+    const int nk = STR ? cur.nk : K / BK;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -702,7 +707,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     block_barrier();
     if (more) {
       setup(nxt, arow_n);
-      prologue(GEN ? nxt.nk : K / BK);
+      prologue(STR ? nxt.nk : K / BK);
     }
     store_tile(cur, smem + (STAGES - 1) * Cfg::kStageBytes + wave * kEpiWaveBytes);
     if (!more) break;

@@ -142,14 +142,14 @@ hipError_t launch_newton_schulz(int64_t n, int64_t R, int64_t C, int64_t steps, 
     const bool last = s + 1 == steps;
     // A = Xw Xw^T
     GemmArgs p1 = batch_gemm(Xw, Xw, Rw * Cw, (int)n, Rw, (int)Rw, (int)Cw, Ab);
-    hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, BK, WM, WN, ST, EPI_STORE, 1, true>), dim3(num_cu),
+    hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, BK, WM, WN, ST, EPI_STORE, 1, kFeatGroups>), dim3(num_cu),
                        dim3(WM * WN * 64), 0, stream, p1);
     // B = c (A A^T) + b A
     GemmArgs p2 = batch_gemm(Ab, Ab, Rw * Rw, (int)n, Rw, (int)Rw, (int)Rw, Bb);
     p2.alpha = c;
     p2.beta = b;
     p2.D = Ab;
-    hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, BK, WM, WN, ST, EPI_AXPBY, 1, true>), dim3(num_cu),
+    hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, BK, WM, WN, ST, EPI_AXPBY, 1, kFeatGroups>), dim3(num_cu),
                        dim3(WM * WN * 64), 0, stream, p2);
     // Xt' = Xt B^T + a Xt; for a tall matrix Xt is the caller's orientation
     bf16* out = (last && tall) ? X : Xt[cur ^ 1];
@@ -157,7 +157,7 @@ hipError_t launch_newton_schulz(int64_t n, int64_t R, int64_t C, int64_t steps, 
     p3.alpha = 1.0f;
     p3.beta = a;
     p3.D = Xt[cur];
-    hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, BK, WM, WN, ST, EPI_AXPBY, 1, true>), dim3(num_cu),
+    hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, BK, WM, WN, ST, EPI_AXPBY, 1, kFeatGroups>), dim3(num_cu),
                        dim3(WM * WN * 64), 0, stream, p3);
     if (last && tall) break;
     // Xw = Xt'^T (the result itself on the last step of a wide matrix)
