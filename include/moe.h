@@ -1,5 +1,6 @@
 /*
- * moe.h - C ABI of the MI355X (gfx950) routed Mixture-of-Experts layer forward.
+ * moe.h - C ABI of the MI355X (gfx950) routed Mixture-of-Experts layer: forward,
+ * backward, and Muon's Newton-Schulz step for whole expert matrices.
  *
  * The layer (one Mixture-of-Experts block of the ~1T-parameter model in
  * "Training a 1T-Parameter MoE on EU public infrastructure with PyTorch and
@@ -169,15 +170,17 @@ moe_status moe_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
  *   dX = dG W_g + dU W_u,  dW_d = dY^T H,  dW_g = dG^T X,  dW_u = dU^T X.
  * G and U are recomputed (nothing from the forward is needed but its inputs).
  *   n_max, d, E, F, x_in, n_in, a_rows, offsets, w_gate, w_up, w_down: as in
- *                        moe_grouped_ffn (dtype MOE_BF16 only)
- *   dy_perm  [n_max,d] bf16    dY, rows grouped by expert (rows offsets[E].. unused)
- *   dx_perm  [n_max,d] bf16    out: dX (first offsets[E] rows written)
+ *                        moe_grouped_ffn
+ *   dy_perm  [n_max,d] dtype   dY, rows grouped by expert (rows offsets[E].. unused)
+ *   dx_perm  [n_max,d] dtype   out: dX (first offsets[E] rows written)
  *   dw_gate, dw_up [E,F,d] f32, dw_down [E,d,F] f32   out; zero for an expert with
  *                        no rows
  *   ws: query with ws == NULL (holds transposed weights, dH in float32, dG|dU,
- *       H and transposed activations: about 3 E d F + n_max (4 + 2 + 2 + 2 + ...) F
- *       + 2 (d + 3 F) (n_max + 63 E) elements).
- * Errors as moe_grouped_ffn; a dtype other than MOE_BF16 is MOE_ERR_UNSUPPORTED.
+ *       H and transposed activations: about 3 E d F + 4 n_max F dtype elements,
+ *       n_max F float32, and 2 (d + 3 F) (n_max + 63 E) dtype elements).
+ * bf16: bf16 products, float32 accumulation; dG, dU and H are rounded to bf16
+ * before the products that use them.  float32: float32 throughout.
+ * Errors as moe_grouped_ffn.
  */
 moe_status moe_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_dtype dtype,
                                     const void* x_in, int64_t n_in, const int32_t* a_rows,
@@ -185,6 +188,99 @@ moe_status moe_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int64_t
                                     const void* w_down, const void* dy_perm, void* dx_perm,
                                     float* dw_gate, float* dw_up, float* dw_down,
                                     void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * Backward of the whole layer.  The pages' workload is pre-training ("Training
+ * a 1T-Parameter MoE on EU public infrastructure with PyTorch and TorchTitan",
+ * TL;DR and "The machine and its constraints"), so every step runs the layer
+ * backward after the forward.  Given the output gradient dy, the chain rule of
+ * the forward above gives, step by step in reverse:
+ *   combine:       dy_perm[slot_row[t,j]] = w[t,j] dy[t]
+ *                  g[t,j] = <dy[t], y_perm[slot_row[t,j]]>          (gradient of w)
+ *   experts:       moe_grouped_ffn_backward on the permuted rows
+ *   gate weights:  w[t,:] is a softmax of the selected logits (the full softmax's
+ *                  denominator cancels when renormalising), so
+ *                  dl[t,S_tj] = w[t,j] (g[t,j] - sum_i w[t,i] g[t,i]); every
+ *                  other logit gets 0 (the selection is piecewise constant)
+ *   router:        dx += dl W_r,  dW_r = dl^T x,  db = sum over tokens of dl
+ *   permutation:   dx[t] += sum_j dx_perm[slot_row[t,j]]
+ * Every reduction runs in a fixed order (no atomics): results are
+ * bit-reproducible for the same inputs and sizes.
+ */
+
+/*
+ * moe_combine_backward: backward of moe_combine.
+ *   dy        [T,d]   dtype    output gradient
+ *   y_perm    [*,d]   dtype    the forward's expert outputs (rows slot_row refers to)
+ *   slot_row  [T,k]   int32    the forward's map (from moe_permute); < 0: skipped slot
+ *   topk_w    [T,k]   float32  the forward's gate weights
+ *   dy_perm   [*,d]   dtype    out: row slot_row[t,j] = topk_w[t,j] dy[t] (float32
+ *                              product, rounded to dtype); rows no slot refers to
+ *                              are left untouched
+ *   d_topk_w  [T,k]   float32  out: g[t,j] = <dy[t], y_perm[slot_row[t,j]]> (float32
+ *                              sum), 0 for a skipped slot
+ * slot_row must hold distinct in-range rows (as moe_permute writes them).  No
+ * workspace.  Errors: sizes <= 0 or null/misaligned pointers:
+ * MOE_ERR_INVALID_ARG; d not a multiple of 64 or T*k >= 2^31: MOE_ERR_UNSUPPORTED.
+ */
+moe_status moe_combine_backward(int64_t T, int64_t d, int64_t k, moe_dtype dtype, const void* dy,
+                                const void* y_perm, const int32_t* slot_row, const float* topk_w,
+                                void* dy_perm, float* d_topk_w, void* stream);
+
+/*
+ * moe_route_backward: backward of moe_route (renormalised top-k softmax and
+ * router GEMM), plus the permutation's backward when dx_perm is given, since both
+ * end in dx.
+ *   x, w_router            as in moe_route
+ *   topk_ids, topk_w [T,k] the forward's routing (ids distinct per token; ids
+ *                          outside [0, E) are skipped)
+ *   d_topk_w  [T,k] f32    gradient of the gate weights (moe_combine_backward's g)
+ *   dx_perm   [*,d] dtype  gradient of the permuted rows, or NULL
+ *   slot_row  [T,k] int32  the forward's map; required exactly when dx_perm is given
+ *   dx        [T,d] dtype  out: sum_j dl[t,j] W_r[ids[t,j]] (+ sum_j dx_perm[slot_row[t,j]])
+ *                          summed in float32, rounded once
+ *   dw_router [E,d] f32    out: dl^T x (bf16: dl rounded to bf16 for the
+ *                          product, float32 accumulation)
+ *   dbias     [E]   f32    out: float32 column sums of dl, or NULL to skip
+ *   dlogits_out [T,E] f32  out: the dense logit gradient dl, or NULL (then it lives
+ *                          in the workspace)
+ *   ws: query with ws == NULL (about T E 4 + (E + d) T' dtype bytes, T' = T rounded
+ *       up to 64, plus up to 16 E d float32 partial sums).
+ * Errors as moe_route; dx_perm given without slot_row or the reverse:
+ * MOE_ERR_INVALID_ARG.
+ */
+moe_status moe_route_backward(int64_t T, int64_t d, int64_t E, int64_t k, moe_dtype dtype,
+                              const void* x, const void* w_router, const int32_t* topk_ids,
+                              const float* topk_w, const float* d_topk_w, const void* dx_perm,
+                              const int32_t* slot_row, void* dx, float* dw_router, float* dbias,
+                              float* dlogits_out, void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * moe_layer_backward: the whole layer backward from the forward's saved routing
+ * and expert outputs.
+ *   T, d, E, k, F, dtype, x, w_router, w_gate, w_up, w_down: as in moe_layer_forward
+ *                          (w_router NULL: pre-routed slots, no router gradient)
+ *   topk_ids, topk_w [T,k] the forward's routing (negative id: slot owned elsewhere)
+ *   y_perm  [T*k,d] dtype  the forward's expert outputs, rows in the permutation's
+ *                          order (experts ascending, tokens ascending within an
+ *                          expert; moe_permute's order, recomputed here from topk_ids)
+ *   dy      [T,d]   dtype  output gradient
+ *   dx      [T,d]   dtype  out: input gradient (experts, permutation and router)
+ *   dw_router [E,d] f32    out (NULL when pre-routed); dbias [E] f32 out or NULL
+ *                          (must be NULL when pre-routed)
+ *   dw_gate, dw_up [E,F,d], dw_down [E,d,F] f32   out (zero for an expert with no rows)
+ *   d_topk_w_out [T,k] f32 out: gradient of the gate weights, or NULL
+ *   ws: query with ws == NULL (the grouped-FFN backward's workspace for T*k rows,
+ *       plus dy_perm and dx_perm, plus moe_route_backward's when routed).
+ * Errors as moe_layer_forward; dw_router or dbias given when pre-routed:
+ * MOE_ERR_INVALID_ARG.
+ */
+moe_status moe_layer_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t F, moe_dtype dtype,
+                              const void* x, const void* w_router, const void* w_gate, const void* w_up,
+                              const void* w_down, const int32_t* topk_ids, const float* topk_w,
+                              const void* y_perm, const void* dy, void* dx, float* dw_router, float* dbias,
+                              float* dw_gate, float* dw_up, float* dw_down, float* d_topk_w_out,
+                              void* ws, size_t* ws_bytes, void* stream);
 
 /*
  * moe_newton_schulz: Muon's orthogonalisation of a batch of whole matrices

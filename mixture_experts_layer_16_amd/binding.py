@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_F32, MOE_BF16 = 0, 1
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
 EXPORTS = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_newton_schulz",
-           "moe_grouped_ffn_backward")
+           "moe_grouped_ffn_backward", "moe_combine_backward", "moe_route_backward", "moe_layer_backward")
 
 
 class MoEError(RuntimeError):
@@ -43,6 +43,11 @@ _SIGS = {
     "moe_newton_schulz": [_i64, _i64, _i64, _int, _i64, _f32, _f32, _f32, _f32, _vp, _vp, _vp, _szp, _vp],
     "moe_grouped_ffn_backward": [_i64, _i64, _i64, _i64, _int, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _vp, _vp, _vp, _szp, _vp],
+    "moe_combine_backward": [_i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_route_backward": [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                           _szp, _vp],
+    "moe_layer_backward": [_i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp],
 }
 
 MUON_COEFFS = (3.4445, -4.7750, 2.0315)
@@ -194,6 +199,82 @@ class GroupedFfnBackward:
 def moe_grouped_ffn_backward(x_in, offsets, w_gate, w_up, w_down, dy_perm, a_rows=None):
     """(dx_perm, dW_gate, dW_up, dW_down) of the grouped SwiGLU FFN."""
     return GroupedFfnBackward(x_in, offsets, w_gate, w_up, w_down, dy_perm, a_rows)()
+
+
+def moe_combine_backward(dy, y_perm, slot_row, topk_w, dy_perm=None):
+    """Backward of moe_combine: returns (dy_perm, d_topk_w).  dy_perm rows that no
+    slot refers to are left as allocated (zero when allocated here)."""
+    T, k = slot_row.shape
+    d = dy.shape[1]
+    dev = dy.device
+    if dy_perm is None:
+        dy_perm = torch.zeros(y_perm.shape[0], d, dtype=dy.dtype, device=dev)
+    g = torch.empty(T, k, dtype=torch.float32, device=dev)
+    _check("moe_combine_backward",
+           lib().moe_combine_backward(T, d, k, dtype_code(dy.dtype), _p(dy), _p(y_perm), _p(slot_row), _p(topk_w),
+                                      _p(dy_perm), _p(g), _stream(dev)))
+    return dy_perm, g
+
+
+def moe_route_backward(x, w_router, topk_ids, topk_w, d_topk_w, dx_perm=None, slot_row=None, want_bias=True,
+                       want_dlogits=False):
+    """Backward of moe_route (plus the permutation's when dx_perm and slot_row are
+    given).  Returns (dx, dW_router, dbias | None, dlogits | None)."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    k = topk_ids.shape[1]
+    dev = x.device
+    dx = torch.empty(T, d, dtype=x.dtype, device=dev)
+    dwr = torch.empty(E, d, dtype=torch.float32, device=dev)
+    db = torch.empty(E, dtype=torch.float32, device=dev) if want_bias else None
+    dl = torch.empty(T, E, dtype=torch.float32, device=dev) if want_dlogits else None
+    head = (T, d, E, k, dtype_code(x.dtype), _p(x), _p(w_router), _p(topk_ids), _p(topk_w), _p(d_topk_w),
+            _p(dx_perm), _p(slot_row), _p(dx), _p(dwr), _p(db), _p(dl))
+    ws = _ws(_query("moe_route_backward", *head), dev)
+    n = ctypes.c_size_t(ws.numel())
+    _check("moe_route_backward", lib().moe_route_backward(*head, _p(ws), ctypes.byref(n), _stream(dev)))
+    return dx, dwr, db, dl
+
+
+class LayerBackward:
+    """moe_layer_backward with its outputs and workspace allocated once.  The
+    forward's routing (topk_ids, topk_w) and expert outputs y_perm (rows in the
+    permutation's order) are inputs; w_router None means pre-routed slots."""
+
+    def __init__(self, x, w_router, w_gate, w_up, w_down, topk_ids, topk_w, y_perm, dy, want_bias: bool = True,
+                 want_d_topk_w: bool = False):
+        T, d = x.shape
+        E, F, _ = w_gate.shape
+        k = topk_ids.shape[1]
+        dev = x.device
+        routed = w_router is not None
+        self.t = (x, w_router, w_gate, w_up, w_down, topk_ids, topk_w, y_perm, dy)
+        self.dx = torch.empty(T, d, dtype=x.dtype, device=dev)
+        self.dw_router = torch.empty(E, d, dtype=torch.float32, device=dev) if routed else None
+        self.dbias = torch.empty(E, dtype=torch.float32, device=dev) if (routed and want_bias) else None
+        self.dw_gate = torch.empty(E, F, d, dtype=torch.float32, device=dev)
+        self.dw_up = torch.empty(E, F, d, dtype=torch.float32, device=dev)
+        self.dw_down = torch.empty(E, d, F, dtype=torch.float32, device=dev)
+        self.d_topk_w = torch.empty(T, k, dtype=torch.float32, device=dev) if want_d_topk_w else None
+        self._head = (T, d, E, k, F, dtype_code(x.dtype), _p(x), _p(w_router), _p(w_gate), _p(w_up), _p(w_down),
+                      _p(topk_ids), _p(topk_w), _p(y_perm), _p(dy), _p(self.dx), _p(self.dw_router),
+                      _p(self.dbias), _p(self.dw_gate), _p(self.dw_up), _p(self.dw_down), _p(self.d_topk_w))
+        self.ws = _ws(_query("moe_layer_backward", *self._head), dev)
+        self._n = ctypes.c_size_t(self.ws.numel())
+        self._ws_p = _p(self.ws)
+
+    def __call__(self):
+        _check("moe_layer_backward", lib().moe_layer_backward(*self._head, self._ws_p, ctypes.byref(self._n),
+                                                              _stream(self.dx.device)))
+        return self
+
+
+def moe_layer_backward(x, w_router, w_gate, w_up, w_down, topk_ids, topk_w, y_perm, dy, want_bias=True,
+                       want_d_topk_w=False):
+    """One call of the whole layer backward; returns the LayerBackward object
+    holding dx, dw_router, dbias, dw_gate, dw_up, dw_down and d_topk_w."""
+    return LayerBackward(x, w_router, w_gate, w_up, w_down, topk_ids, topk_w, y_perm, dy, want_bias,
+                         want_d_topk_w)()
 
 
 class NewtonSchulz:

@@ -8,35 +8,11 @@
 // is bit-reproducible.  Negative rows (slots owned elsewhere) contribute 0.
 #include "common.h"
 #include "kernels.h"
+#include "rows.h"
 
 namespace moe {
 
 namespace {
-
-__device__ __forceinline__ void load8(const bf16* p, float* v) {
-  const bf16x8 q = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = static_cast<float>(q[i]);
-}
-__device__ __forceinline__ void store8(bf16* p, const float* v) {
-  bf16x8 q;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = static_cast<bf16>(v[i]);
-  *reinterpret_cast<bf16x8*>(p) = q;
-}
-__device__ __forceinline__ void load8(const float* p, float* v) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[i + 4] = b[i]; }
-}
-__device__ __forceinline__ void store8(float* p, const float* v) {
-  f32x4 a, b;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { a[i] = v[i]; b[i] = v[i + 4]; }
-  *reinterpret_cast<f32x4*>(p) = a;
-  *reinterpret_cast<f32x4*>(p + 4) = b;
-}
 
 // KU > 0: k is the compile-time KU, so the token's KU row loads are all in
 // flight before the first FMA; KU == 0: any k, in groups of 8.

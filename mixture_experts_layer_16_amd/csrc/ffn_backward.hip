@@ -14,6 +14,8 @@
 //   * dH = dY (W_d^T)^T and dX = [dG | dU] [W_g^T ; W_u^T]^T read transposed
 //     copies of the weights ([E, F, d] and [E, d, 2F], made here, bandwidth-
 //     bound), in float32 (dH) and the I/O type (dX);
+//   * the I/O type is bf16 (MFMA bf16 products, float32 accumulation) or float32
+//     (float32 MFMA products throughout);
 //   * G and U are recomputed by the gate/up GEMM, whose epilogue turns them and
 //     dH into dG, dU (one [n, 2F] buffer) and H;
 //   * the weight gradients contract over each expert's rows: the activations
@@ -127,15 +129,11 @@ void gemm(const GemmArgs& a, int num_cu, hipStream_t s) {
   hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, 4, 2, 2, EPI, 1, FEAT>), dim3(num_cu), dim3(512), 0, s, a);
 }
 
-}  // namespace
-
-hipError_t launch_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_in,
-                                       const int32_t* a_rows, const int32_t* offsets, const void* w_gate,
-                                       const void* w_up, const void* w_down, const void* dy_perm, void* dx_perm,
-                                       float* dw_gate, float* dw_up, float* dw_down, const FfnBackwardScratch& w,
-                                       int num_cu, hipStream_t s) {
-  typedef bf16 T;
-  constexpr int BK = 64;
+template <typename T, int BK>
+hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_in, const int32_t* a_rows,
+                          const int32_t* offsets, const void* w_gate, const void* w_up, const void* w_down,
+                          const void* dy_perm, void* dx_perm, float* dw_gate, float* dw_up, float* dw_down,
+                          const FfnBackwardScratch& w, int num_cu, hipStream_t s) {
   const int64_t np = w.n_pad;   // columns of the padded transposed layouts
   const T* Wg = static_cast<const T*>(w_gate);
   const T* Wu = static_cast<const T*>(w_up);
@@ -192,6 +190,20 @@ hipError_t launch_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int6
   wgrad(w.dg_t, (int)F, w.x_t, (int)d, dw_gate);
   wgrad(w.du_t, (int)F, w.x_t, (int)d, dw_up);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_grouped_ffn_backward(int dtype, int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_in,
+                                       const int32_t* a_rows, const int32_t* offsets, const void* w_gate,
+                                       const void* w_up, const void* w_down, const void* dy_perm, void* dx_perm,
+                                       float* dw_gate, float* dw_up, float* dw_down, const FfnBackwardScratch& w,
+                                       int num_cu, hipStream_t s) {
+  if (dtype == 1)
+    return ffn_backward_t<bf16, 64>(n_max, d, E, F, x_in, a_rows, offsets, w_gate, w_up, w_down, dy_perm, dx_perm,
+                                    dw_gate, dw_up, dw_down, w, num_cu, s);
+  return ffn_backward_t<float, 32>(n_max, d, E, F, x_in, a_rows, offsets, w_gate, w_up, w_down, dy_perm, dx_perm,
+                                   dw_gate, dw_up, dw_down, w, num_cu, s);
 }
 
 }  // namespace moe

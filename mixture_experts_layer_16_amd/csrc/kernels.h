@@ -40,23 +40,23 @@ hipError_t launch_newton_schulz(int64_t n, int64_t R, int64_t C, int64_t steps, 
                                 float eps, const void* g, void* x, void* xw, void* xt0, void* xt1, void* A,
                                 void* B, float* partial, int num_cu, hipStream_t stream);
 
-// Backward of the grouped SwiGLU FFN (bf16): dx_perm and the float32 weight
-// gradients from dy_perm.  Scratch (caller-carved):
+// Backward of the grouped SwiGLU FFN: dx_perm and the float32 weight gradients
+// from dy_perm.  Scratch (caller-carved; "I/O" = the dtype's element type):
 struct FfnBackwardScratch {
   int32_t* poff;   // [E+1] padded expert column offsets
-  void* wd_t;      // [E, F, d]   W_d transposed
-  void* wgu_t;     // [E, d, 2F]  W_g and W_u transposed, side by side
+  void* wd_t;      // [E, F, d]   W_d transposed (I/O)
+  void* wgu_t;     // [E, d, 2F]  W_g and W_u transposed, side by side (I/O)
   float* dh;       // [n_max, F]  dH (float32)
-  void* dgu;       // [n_max, 2F] dG | dU
-  void* h;         // [n_max, F]  H recomputed
-  void* x_t;       // [d, n_pad]  expert rows of the input, transposed and padded
-  void* dy_t;      // [d, n_pad]
-  void* h_t;       // [F, n_pad]
-  void* dg_t;      // [F, n_pad]
-  void* du_t;      // [F, n_pad]
+  void* dgu;       // [n_max, 2F] dG | dU (I/O)
+  void* h;         // [n_max, F]  H recomputed (I/O)
+  void* x_t;       // [d, n_pad]  expert rows of the input, transposed and padded (I/O)
+  void* dy_t;      // [d, n_pad]  (I/O)
+  void* h_t;       // [F, n_pad]  (I/O)
+  void* dg_t;      // [F, n_pad]  (I/O)
+  void* du_t;      // [F, n_pad]  (I/O)
   int64_t n_pad;   // >= sum over experts of rows rounded up to 64; a multiple of 64
 };
-hipError_t launch_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_in,
+hipError_t launch_grouped_ffn_backward(int dtype, int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_in,
                                        const int32_t* a_rows, const int32_t* offsets, const void* w_gate,
                                        const void* w_up, const void* w_down, const void* dy_perm, void* dx_perm,
                                        float* dw_gate, float* dw_up, float* dw_down, const FfnBackwardScratch& w,
@@ -65,5 +65,37 @@ hipError_t launch_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int6
 // Weighted un-permute: y[t] = sum_j w[t,j] * y_perm[slot_row[t,j]].
 hipError_t launch_combine(int dtype, int64_t T, int64_t d, int64_t k, const void* y_perm,
                           const int32_t* slot_row, const float* w, void* y, hipStream_t stream);
+
+// Backward of the combine: dy_perm[slot_row[t,j]] = w[t,j] dy[t] and
+// g[t,j] = <dy[t], y_perm[slot_row[t,j]]> (0 for slot_row < 0).
+hipError_t launch_combine_backward(int dtype, int64_t T, int64_t d, int64_t k, const void* dy, const void* y_perm,
+                                   const int32_t* slot_row, const float* w, void* dy_perm, float* g,
+                                   hipStream_t stream);
+
+// Backward of the routing (renormalised top-k softmax and router GEMM) plus the
+// permutation: dx[t] = sum_j dl[t,j] W_r[ids[t,j]] + sum_j dx_perm[slot_row[t,j]]
+// (dx_perm == nullptr: router part only), dW_r = dl^T x, db = column sums of dl
+// (dbias == nullptr: skipped).  Scratch (caller-carved):
+constexpr int kMaxSplits = 16;
+struct RouteBackwardScratch {
+  float* dlogits;        // [T, E] dense logit gradient
+  void* dl_t;            // [E, t_pad] its transpose (I/O type)
+  void* x_t;             // [d, t_pad] x transposed (I/O type)
+  int32_t* kseg;         // [splits + 1] token ranges of the split GEMM
+  float* split_partial;  // [splits, E, d] when splits > 1
+  float* bias_partial;   // [bias_chunks, E]
+  int64_t t_pad;         // T rounded up to 64
+  int splits;            // 1 .. kMaxSplits (route_backward_splits)
+  int bias_chunks;       // 1 .. 64
+};
+int route_backward_splits(int64_t E, int64_t d, int64_t t_pad);
+hipError_t launch_route_backward(int dtype, int64_t T, int64_t d, int64_t E, int64_t k, const void* x,
+                                 const void* w_router, const int32_t* ids, const float* w, const float* g,
+                                 const void* dx_perm, const int32_t* slot_row, void* dx, float* dw_router,
+                                 float* dbias, const RouteBackwardScratch& ws, int num_cu, hipStream_t stream);
+
+// Backward of the permutation alone: dx[t] = sum_j dx_perm[slot_row[t,j]].
+hipError_t launch_unpermute(int dtype, int64_t T, int64_t d, int64_t k, const void* dx_perm,
+                            const int32_t* slot_row, void* dx, hipStream_t stream);
 
 }  // namespace moe

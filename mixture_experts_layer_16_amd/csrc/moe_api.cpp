@@ -1,4 +1,4 @@
-// C ABI of the routed-MoE layer forward: argument checks, workspace sizing and
+// C ABI of the routed-MoE layer (forward, backward, Muon's Newton-Schulz): argument checks, workspace sizing and
 // carving, launch geometry.  All checks run on the host before any HIP call, so
 // a bad call returns a status without touching the device.  Kernels are only
 // enqueued on the caller's stream; nothing here synchronises or allocates.
@@ -107,6 +107,41 @@ struct Carver {
   }
 };
 
+// Scratch of the grouped-FFN backward for n_max rows (element size es).
+void carve_ffn_backward(Carver& c, moe::FfnBackwardScratch& w, int64_t n_max, int64_t d, int64_t E, int64_t F,
+                        size_t es) {
+  const int64_t n_pad = (n_max + 63 * E + 63) / 64 * 64;
+  w.poff = static_cast<int32_t*>(c.take((size_t)(E + 1) * 4));
+  w.wd_t = c.take((size_t)E * F * d * es);
+  w.wgu_t = c.take((size_t)E * d * 2 * F * es);
+  w.dh = static_cast<float*>(c.take((size_t)n_max * F * 4));
+  w.dgu = c.take((size_t)n_max * 2 * F * es);
+  w.h = c.take((size_t)n_max * F * es);
+  w.x_t = c.take((size_t)d * n_pad * es);
+  w.dy_t = c.take((size_t)d * n_pad * es);
+  w.h_t = c.take((size_t)F * n_pad * es);
+  w.dg_t = c.take((size_t)F * n_pad * es);
+  w.du_t = c.take((size_t)F * n_pad * es);
+  w.n_pad = n_pad;
+}
+
+bool ffn_backward_fits(int64_t n_max, int64_t E) { return (n_max + 63 * E + 63) / 64 * 64 < kIdxLimit; }
+
+// Scratch of the routing backward for T tokens (dlogits_out: the caller's buffer).
+void carve_route_backward(Carver& c, moe::RouteBackwardScratch& w, int64_t T, int64_t d, int64_t E, size_t es,
+                          float* dlogits_out) {
+  const int64_t tp = (T + 63) / 64 * 64;
+  w.t_pad = tp;
+  w.splits = moe::route_backward_splits(E, d, tp);
+  w.bias_chunks = (int)(T < 64 ? T : 64);
+  w.dlogits = dlogits_out ? dlogits_out : static_cast<float*>(c.take((size_t)T * E * 4));
+  w.dl_t = c.take((size_t)E * tp * es);
+  w.x_t = c.take((size_t)d * tp * es);
+  w.kseg = static_cast<int32_t*>(c.take((size_t)(moe::kMaxSplits + 1) * 4));
+  w.split_partial = w.splits > 1 ? static_cast<float*>(c.take((size_t)w.splits * E * d * 4)) : nullptr;
+  w.bias_partial = static_cast<float*>(c.take((size_t)w.bias_chunks * E * 4));
+}
+
 }  // namespace
 
 extern "C" {
@@ -185,30 +220,16 @@ moe_status moe_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int64_t
                                     size_t* ws_bytes, void* stream) {
   moe_status st = check_ffn_dims(n_max, d, E, F);
   if (st != MOE_OK) return st;
-  if (dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_dtype(dtype)) != MOE_OK) return st;
+  const size_t es = elem_size(dtype);
   if (a_rows != nullptr) {
     if (n_in <= 0) return MOE_ERR_INVALID_ARG;
-    if ((uint64_t)n_in * (uint64_t)d * 2 >= (uint64_t(1) << 32)) return MOE_ERR_UNSUPPORTED;
+    if ((uint64_t)n_in * (uint64_t)d * es >= (uint64_t(1) << 32)) return MOE_ERR_UNSUPPORTED;
   }
-  const int64_t n_pad = (n_max + 63 * E + 63) / 64 * 64;
-  if (n_pad >= kIdxLimit) return MOE_ERR_UNSUPPORTED;
-  auto carve = [&](Carver& c, moe::FfnBackwardScratch& w) {
-    w.poff = static_cast<int32_t*>(c.take((size_t)(E + 1) * 4));
-    w.wd_t = c.take((size_t)E * F * d * 2);
-    w.wgu_t = c.take((size_t)E * d * 2 * F * 2);
-    w.dh = static_cast<float*>(c.take((size_t)n_max * F * 4));
-    w.dgu = c.take((size_t)n_max * 2 * F * 2);
-    w.h = c.take((size_t)n_max * F * 2);
-    w.x_t = c.take((size_t)d * n_pad * 2);
-    w.dy_t = c.take((size_t)d * n_pad * 2);
-    w.h_t = c.take((size_t)F * n_pad * 2);
-    w.dg_t = c.take((size_t)F * n_pad * 2);
-    w.du_t = c.take((size_t)F * n_pad * 2);
-    w.n_pad = n_pad;
-  };
+  if (!ffn_backward_fits(n_max, E)) return MOE_ERR_UNSUPPORTED;
   moe::FfnBackwardScratch w{};
   Carver c0(nullptr);
-  carve(c0, w);
+  carve_ffn_backward(c0, w, n_max, d, E, F, es);
   const size_t need = c0.used;
   if (ws == nullptr && ws_bytes != nullptr) {
     *ws_bytes = need;
@@ -221,10 +242,130 @@ moe_status moe_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int64_t
   int ncu = 0;
   if ((st = num_cu(&ncu)) != MOE_OK) return st;
   Carver cv(ws);
-  carve(cv, w);
-  return hip_status(moe::launch_grouped_ffn_backward(n_max, d, E, F, x_in, a_rows, offsets, w_gate, w_up, w_down,
-                                                     dy_perm, dx_perm, dw_gate, dw_up, dw_down, w, ncu,
+  carve_ffn_backward(cv, w, n_max, d, E, F, es);
+  return hip_status(moe::launch_grouped_ffn_backward(dtype, n_max, d, E, F, x_in, a_rows, offsets, w_gate, w_up,
+                                                     w_down, dy_perm, dx_perm, dw_gate, dw_up, dw_down, w, ncu,
                                                      static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_combine_backward(int64_t T, int64_t d, int64_t k, moe_dtype dtype, const void* dy,
+                                const void* y_perm, const int32_t* slot_row, const float* topk_w, void* dy_perm,
+                                float* d_topk_w, void* stream) {
+  if (T <= 0 || d <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
+  if (d % 64 != 0 || d > kMaxDim || T * k >= kIdxLimit) return MOE_ERR_UNSUPPORTED;
+  moe_status st = check_dtype(dtype);
+  if (st != MOE_OK) return st;
+  if (!ok16(dy) || !ok16(y_perm) || !ok4(slot_row) || !ok4(topk_w) || !ok16(dy_perm) || !ok4(d_topk_w))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine_backward(dtype, T, d, k, dy, y_perm, slot_row, topk_w, dy_perm, d_topk_w,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_route_backward(int64_t T, int64_t d, int64_t E, int64_t k, moe_dtype dtype, const void* x,
+                              const void* w_router, const int32_t* topk_ids, const float* topk_w,
+                              const float* d_topk_w, const void* dx_perm, const int32_t* slot_row, void* dx,
+                              float* dw_router, float* dbias, float* dlogits_out, void* ws, size_t* ws_bytes,
+                              void* stream) {
+  moe_status st = check_tdek(T, d, E, k);
+  if (st != MOE_OK) return st;
+  if ((st = check_dtype(dtype)) != MOE_OK) return st;
+  const size_t es = elem_size(dtype);
+  moe::RouteBackwardScratch w{};
+  Carver c0(nullptr);
+  carve_route_backward(c0, w, T, d, E, es, dlogits_out);
+  const size_t need = c0.used;
+  if (ws == nullptr && ws_bytes != nullptr) {
+    *ws_bytes = need;
+    return MOE_OK;
+  }
+  if (!ok16(x) || !ok16(w_router) || !ok4(topk_ids) || !ok4(topk_w) || !ok4(d_topk_w) || !ok16(dx) ||
+      !ok16(dw_router) || !opt4(dbias) || !opt16(dlogits_out) || !opt16(dx_perm) || !opt4(slot_row))
+    return MOE_ERR_INVALID_ARG;
+  if ((dx_perm == nullptr) != (slot_row == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (workspace_step(ws, ws_bytes, need, &st)) return st;
+  int ncu = 0;
+  if ((st = num_cu(&ncu)) != MOE_OK) return st;
+  Carver cv(ws);
+  carve_route_backward(cv, w, T, d, E, es, dlogits_out);
+  return hip_status(moe::launch_route_backward(dtype, T, d, E, k, x, w_router, topk_ids, topk_w, d_topk_w, dx_perm,
+                                               slot_row, dx, dw_router, dbias, w, ncu,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_layer_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t F, moe_dtype dtype,
+                              const void* x, const void* w_router, const void* w_gate, const void* w_up,
+                              const void* w_down, const int32_t* topk_ids, const float* topk_w, const void* y_perm,
+                              const void* dy, void* dx, float* dw_router, float* dbias, float* dw_gate, float* dw_up,
+                              float* dw_down, float* d_topk_w_out, void* ws, size_t* ws_bytes, void* stream) {
+  moe_status st = check_tdek(T, d, E, k);
+  if (st != MOE_OK) return st;
+  if (F <= 0) return MOE_ERR_INVALID_ARG;
+  if (F % 64 != 0 || F > kMaxDim) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_dtype(dtype)) != MOE_OK) return st;
+  const bool routed = w_router != nullptr;
+  const size_t es = elem_size(dtype);
+  const int64_t slots = T * k;
+  if (!ffn_backward_fits(slots, E)) return MOE_ERR_UNSUPPORTED;
+  // token rows read in place through row_token when x's byte size fits the GEMM's
+  // 32-bit row offsets; otherwise they are first copied to x_perm
+  const bool in_place = (uint64_t)T * (uint64_t)d * es < (uint64_t(1) << 32);
+
+  moe::FfnBackwardScratch fw{};
+  moe::RouteBackwardScratch rw{};
+  auto carve = [&](Carver& c, int32_t*& offsets, int32_t*& row_token, int32_t*& slot_row, int32_t*& counts,
+                   float*& g, void*& dy_perm, void*& dx_perm, void*& x_perm) {
+    offsets = static_cast<int32_t*>(c.take((size_t)(E + 1) * 4));
+    row_token = static_cast<int32_t*>(c.take((size_t)slots * 4));
+    slot_row = static_cast<int32_t*>(c.take((size_t)slots * 4));
+    counts = static_cast<int32_t*>(c.take(permute_ws(T, E)));
+    g = d_topk_w_out ? d_topk_w_out : static_cast<float*>(c.take((size_t)slots * 4));
+    dy_perm = c.take((size_t)slots * d * es);
+    dx_perm = c.take((size_t)slots * d * es);
+    x_perm = in_place ? nullptr : c.take((size_t)slots * d * es);
+    carve_ffn_backward(c, fw, slots, d, E, F, es);
+    if (routed) carve_route_backward(c, rw, T, d, E, es, nullptr);
+  };
+  int32_t *offsets, *row_token, *slot_row, *counts;
+  float* g;
+  void *dy_perm, *dx_perm, *x_perm;
+  Carver c0(nullptr);
+  carve(c0, offsets, row_token, slot_row, counts, g, dy_perm, dx_perm, x_perm);
+  const size_t need = c0.used;
+  if (ws == nullptr && ws_bytes != nullptr) {
+    *ws_bytes = need;
+    return MOE_OK;
+  }
+  if (!ok16(x) || !ok16(w_gate) || !ok16(w_up) || !ok16(w_down) || !ok4(topk_ids) || !ok4(topk_w) ||
+      !ok16(y_perm) || !ok16(dy) || !ok16(dx) || !ok16(dw_gate) || !ok16(dw_up) || !ok16(dw_down) ||
+      !opt4(d_topk_w_out))
+    return MOE_ERR_INVALID_ARG;
+  if (routed) {
+    if (!ok16(w_router) || !ok16(dw_router) || !opt4(dbias)) return MOE_ERR_INVALID_ARG;
+  } else {
+    if (dw_router || dbias) return MOE_ERR_INVALID_ARG;
+  }
+  if (workspace_step(ws, ws_bytes, need, &st)) return st;
+  int ncu = 0;
+  if ((st = num_cu(&ncu)) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver cv(ws);
+  carve(cv, offsets, row_token, slot_row, counts, g, dy_perm, dx_perm, x_perm);
+
+  if ((st = hip_status(moe::launch_permute(dtype, T, d, E, k, x, topk_ids, offsets, row_token, slot_row, x_perm,
+                                           counts, s))) != MOE_OK)
+    return st;
+  if ((st = hip_status(moe::launch_combine_backward(dtype, T, d, k, dy, y_perm, slot_row, topk_w, dy_perm, g, s))) !=
+      MOE_OK)
+    return st;
+  if ((st = hip_status(moe::launch_grouped_ffn_backward(dtype, slots, d, E, F, in_place ? x : x_perm,
+                                                        in_place ? row_token : nullptr, offsets, w_gate, w_up,
+                                                        w_down, dy_perm, dx_perm, dw_gate, dw_up, dw_down, fw, ncu,
+                                                        s))) != MOE_OK)
+    return st;
+  if (routed)
+    return hip_status(moe::launch_route_backward(dtype, T, d, E, k, x, w_router, topk_ids, topk_w, g, dx_perm,
+                                                 slot_row, dx, dw_router, dbias, rw, ncu, s));
+  return hip_status(moe::launch_unpermute(dtype, T, d, k, dx_perm, slot_row, dx, s));
 }
 
 moe_status moe_newton_schulz(int64_t n, int64_t R, int64_t C, moe_dtype dtype, int64_t steps, float a, float b,

@@ -17,6 +17,11 @@ here, so every tensor is drawn from a fixed distribution:
                          multinomial; a token's slots hold distinct experts in
                          ascending order, -1 elsewhere; gate weights ~ U(0, 1)
                          normalised over the token's local slots
+  backward inputs        output gradient dy ~ N(0, 1); where a routing table is
+                         drawn rather than computed: k distinct experts per token
+                         sampled without replacement with probability
+                         proportional to 1/rank_e (Zipf), gate weights ~ U(0.05, 1)
+                         normalised and sorted in descending order
 
 bf16 tensors are the fp32 draws rounded to nearest even.  Tensors are drawn on
 the requested device with torch's generator for that device; the discrete
@@ -132,6 +137,29 @@ def pre_routed_slots(T: int, E: int, k: int, n_slots: int, n_empty: int, hot_fra
     s = w.sum(axis=1, keepdims=True)
     w = np.divide(w, s, out=np.zeros_like(w), where=s > 0).astype(np.float32)
     return ids, w
+
+
+def synthetic_routing(T: int, E: int, k: int, seed: int):
+    """Seeded routing table (ids [T, k] int32, distinct per token; gate weights
+    [T, k] float32, each row summing to one and non-increasing).  Experts are
+    drawn without replacement with probability proportional to 1/rank_e (ranks a
+    seeded permutation of 1..E), by adding Gumbel noise to the log-probabilities
+    and keeping the k largest."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 3])))
+    ranks = rng.permutation(E) + 1
+    logp = -np.log(ranks.astype(np.float64))
+    keys = logp[None, :] + rng.gumbel(size=(T, E))
+    ids = np.argsort(-keys, axis=1, kind="stable")[:, :k].astype(np.int32)
+    w = rng.uniform(0.05, 1.0, (T, k))
+    w = -np.sort(-(w / w.sum(axis=1, keepdims=True)), axis=1)
+    return ids, w.astype(np.float32)
+
+
+def output_grad(T: int, d: int, dtype, device="cuda", seed: int = 0) -> torch.Tensor:
+    """Seeded output gradient dy [T, d] ~ N(0, 1) in dtype."""
+    gen = torch.Generator(device=torch.device(device))
+    gen.manual_seed(seed + 7919)
+    return _normal((T, d), 1.0, gen, torch.device(device), dtype)
 
 
 def make_inputs(wl: Workload, device="cuda", seed: Optional[int] = None) -> dict:

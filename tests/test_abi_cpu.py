@@ -25,7 +25,7 @@ def declared_symbols():
     return sorted(set(re.findall(r"^moe_status\s+(moe_\w+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_five_entry_points():
+def test_header_declares_every_exported_entry_point():
     assert declared_symbols() == sorted(B.EXPORTS)
 
 
@@ -221,18 +221,19 @@ def test_newton_schulz_argument_errors(kw, status):
 
 # ---- expert-FFN backward --------------------------------------------------------
 
-def bwd_ws(n_max, d, E, F):
+def bwd_ws(n_max, d, E, F, es=2):
     n_pad = (n_max + 63 * E + 63) // 64 * 64
-    return (ru((E + 1) * 4) + ru(E * F * d * 2) + ru(E * d * 2 * F * 2) + ru(n_max * F * 4) + ru(n_max * 2 * F * 2)
-            + ru(n_max * F * 2) + 2 * ru(d * n_pad * 2) + 3 * ru(F * n_pad * 2))
+    return (ru((E + 1) * 4) + ru(E * F * d * es) + ru(E * d * 2 * F * es) + ru(n_max * F * 4)
+            + ru(n_max * 2 * F * es) + ru(n_max * F * es) + 2 * ru(d * n_pad * es) + 3 * ru(F * n_pad * es))
 
 
-@pytest.mark.parametrize("n_max,d,E,F", [(1000, 128, 4, 192), (524288, 6144, 384, 1792), (64, 64, 1, 64)])
-def test_ffn_backward_workspace_query(n_max, d, E, F):
+@pytest.mark.parametrize("n_max,d,E,F,dt", [(1000, 128, 4, 192, 1), (524288, 6144, 384, 1792, 1), (64, 64, 1, 64, 1),
+                                            (512, 128, 16, 64, 0)])
+def test_ffn_backward_workspace_query(n_max, d, E, F, dt):
     nb = ctypes.c_size_t(12345)
-    st = B.lib().moe_grouped_ffn_backward(n_max, d, E, F, 1, P, 0, None, P, P, P, P, P, P, P, P, P, None,
+    st = B.lib().moe_grouped_ffn_backward(n_max, d, E, F, dt, P, 0, None, P, P, P, P, P, P, P, P, P, None,
                                           ctypes.byref(nb), None)
-    assert st == OK and nb.value == bwd_ws(n_max, d, E, F)
+    assert st == OK and nb.value == bwd_ws(n_max, d, E, F, 2 if dt == 1 else 4)
 
 
 def bwd(n_max=1000, d=128, E=4, F=128, dt=1, xp=P, n_in=0, rows=None, off=P, wg=P, wu=P, wd=P, dy=P, dx=P,
@@ -244,7 +245,7 @@ def bwd(n_max=1000, d=128, E=4, F=128, dt=1, xp=P, n_in=0, rows=None, off=P, wg=
 
 @pytest.mark.parametrize("kw,status", [
     (dict(n_max=0), INVALID), (dict(F=0), INVALID), (dict(F=100), UNSUPPORTED), (dict(d=65), UNSUPPORTED),
-    (dict(E=2000), UNSUPPORTED), (dict(dt=0), UNSUPPORTED), (dict(dt=9), UNSUPPORTED),
+    (dict(E=2000), UNSUPPORTED), (dict(dt=9), UNSUPPORTED),
     (dict(xp=None), INVALID), (dict(off=None), INVALID), (dict(dy=P_MIS), INVALID), (dict(dx=None), INVALID),
     (dict(dwg=P_MIS), INVALID), (dict(dwd=None), INVALID), (dict(nbytes=1000), WORKSPACE),
     (dict(rows=P, n_in=0), INVALID), (dict(rows=P, n_in=(1 << 31) // 128), UNSUPPORTED),
@@ -252,3 +253,108 @@ def bwd(n_max=1000, d=128, E=4, F=128, dt=1, xp=P, n_in=0, rows=None, off=P, wg=
 ])
 def test_ffn_backward_argument_errors(kw, status):
     assert bwd(**kw) == status
+
+
+# ---- layer backward: combine, routing, whole layer --------------------------------
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 128, 2, 1, P, P, P, P, P, P), INVALID), ((10, 100, 2, 1, P, P, P, P, P, P), UNSUPPORTED),
+    ((10, 128, 2, 3, P, P, P, P, P, P), UNSUPPORTED), ((10, 128, 0, 1, P, P, P, P, P, P), INVALID),
+    ((10, 128, 2, 1, None, P, P, P, P, P), INVALID), ((10, 128, 2, 1, P, P, P, P, P_MIS, P), INVALID),
+    ((10, 128, 2, 1, P, P, P, P, P, None), INVALID), ((1 << 28, 128, 8, 1, P, P, P, P, P, P), UNSUPPORTED),
+])
+def test_combine_backward_argument_errors(args, status):
+    assert B.lib().moe_combine_backward(*args, None) == status
+
+
+def route_splits(E, d, tp):
+    tiles = -(-E // 256) * -(-d // 256)
+    s = min(-(-256 // tiles), max(1, tp // 64 // 4))
+    return max(1, min(s, 16))
+
+
+def route_bwd_ws(T, d, E, es=2, dlogits_given=False):
+    tp = (T + 63) // 64 * 64
+    sp = route_splits(E, d, tp)
+    n = 0 if dlogits_given else ru(T * E * 4)
+    n += ru(E * tp * es) + ru(d * tp * es) + ru(17 * 4) + (ru(sp * E * d * 4) if sp > 1 else 0)
+    return n + ru(min(T, 64) * E * 4)
+
+
+@pytest.mark.parametrize("T,d,E,k,dt", [(256, 128, 16, 2, 0), (4096, 1024, 64, 8, 1), (65536, 6144, 384, 8, 1),
+                                        (100, 64, 5, 2, 1), (1, 64, 1, 1, 0)])
+def test_route_backward_workspace_query(T, d, E, k, dt):
+    for given in (False, True):
+        nb = ctypes.c_size_t(12345)
+        st = B.lib().moe_route_backward(T, d, E, k, dt, P, P, P, P, P, None, None, P, P, None, P if given else None,
+                                        None, ctypes.byref(nb), None)
+        assert st == OK and nb.value == route_bwd_ws(T, d, E, 2 if dt == 1 else 4, given)
+
+
+def test_route_backward_splits_fill_the_chip_at_the_page_shape():
+    # 2 x 24 output tiles of 256 x 256, split 6 ways over tokens
+    assert route_splits(384, 6144, 65536) == 6
+    assert route_splits(16, 128, 256) == 1
+
+
+def rbwd(T=100, d=128, E=8, k=2, dt=1, x=P, wr=P, ids=P, w=P, g=P, dxp=None, sr=None, dx=P, dwr=P, db=None, dl=None,
+         ws=P, nbytes=1 << 30):
+    nb = ctypes.c_size_t(nbytes)
+    return B.lib().moe_route_backward(T, d, E, k, dt, x, wr, ids, w, g, dxp, sr, dx, dwr, db, dl, ws, ctypes.byref(nb),
+                                      None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), INVALID), (dict(k=9), INVALID), (dict(d=96), UNSUPPORTED), (dict(E=1025, k=2), UNSUPPORTED),
+    (dict(dt=3), UNSUPPORTED), (dict(x=None), INVALID), (dict(wr=P_MIS), INVALID), (dict(g=None), INVALID),
+    (dict(dwr=None), INVALID), (dict(dx=None), INVALID), (dict(db=P_MIS), INVALID), (dict(dl=P_MIS), INVALID),
+    (dict(dxp=P), INVALID), (dict(sr=P), INVALID), (dict(dxp=P_MIS, sr=P), INVALID), (dict(nbytes=1000), WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x10010)), INVALID),
+])
+def test_route_backward_argument_errors(kw, status):
+    assert rbwd(**kw) == status
+
+
+def layer_bwd_ws(T, d, E, k, F, es, routed=True, g_given=False):
+    slots = T * k
+    n = ru((E + 1) * 4) + 2 * ru(slots * 4) + ru(-(-T // 256) * E * 4)
+    n += 0 if g_given else ru(slots * 4)
+    n += 2 * ru(slots * d * es)
+    if T * d * es >= 1 << 32:
+        n += ru(slots * d * es)
+    n += bwd_ws(slots, d, E, F, es)
+    return n + (route_bwd_ws(T, d, E, es) if routed else 0)
+
+
+@pytest.mark.parametrize("T,d,E,k,F,dt", [(256, 128, 16, 2, 64, 0), (4096, 1024, 64, 8, 512, 1),
+                                          (65536, 6144, 384, 8, 1792, 1), (8192, 6144, 384, 8, 1792, 1),
+                                          (400000, 6144, 8, 1, 64, 1)])
+def test_layer_backward_workspace_query(T, d, E, k, F, dt):
+    es = 2 if dt == 1 else 4
+    for routed in (True, False):
+        for g_given in (False, True):
+            nb = ctypes.c_size_t(12345)
+            st = B.lib().moe_layer_backward(T, d, E, k, F, dt, P, P if routed else None, P, P, P, P, P, P, P, P,
+                                            P if routed else None, None, P, P, P, P if g_given else None, None,
+                                            ctypes.byref(nb), None)
+            assert st == OK and nb.value == layer_bwd_ws(T, d, E, k, F, es, routed, g_given)
+
+
+def lbwd(T=64, d=128, E=8, k=2, F=128, dt=1, x=P, wr=P, wg=P, wu=P, wd=P, ids=P, w=P, yp=P, dy=P, dx=P, dwr=P,
+         db=None, dwg=P, dwu=P, dwd=P, g=None, ws=P, nbytes=1 << 34):
+    nb = ctypes.c_size_t(nbytes)
+    return B.lib().moe_layer_backward(T, d, E, k, F, dt, x, wr, wg, wu, wd, ids, w, yp, dy, dx, dwr, db, dwg, dwu,
+                                      dwd, g, ws, ctypes.byref(nb), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), INVALID), (dict(F=0), INVALID), (dict(F=96), UNSUPPORTED), (dict(k=9), INVALID),
+    (dict(d=65), UNSUPPORTED), (dict(dt=2), UNSUPPORTED), (dict(yp=None), INVALID), (dict(dy=P_MIS), INVALID),
+    (dict(dx=None), INVALID), (dict(dwg=None), INVALID), (dict(ids=None), INVALID), (dict(w=P_MIS), INVALID),
+    (dict(dwr=None), INVALID), (dict(g=P_MIS), INVALID),
+    # pre-routed: no router gradients may be asked for
+    (dict(wr=None), INVALID), (dict(wr=None, dwr=None, db=P), INVALID),
+    (dict(nbytes=1000), WORKSPACE), (dict(ws=ctypes.c_void_p(0x10010)), INVALID),
+])
+def test_layer_backward_argument_errors(kw, status):
+    assert lbwd(**kw) == status
