@@ -12,8 +12,10 @@ the bf16 dense MFMA peak; `stages_ms` gives each step's average duration from
 a second, stage-by-stage pass; `cpu_baseline` times the float64 CPU oracle on a
 bounded slice of the same workload.
 
-`--path backward` measures the grouped expert-FFN backward (dX and the three
-weight gradients from dY) on the routing of the same workload.
+`--path backward` measures the layer backward (moe_layer_backward: combine,
+grouped expert FFN, gate-weight/router and permutation backward) from the
+forward's routing and expert outputs of the same workload; its roofline covers
+the grouped expert-FFN backward, timed alone in a stage-by-stage pass.
 
 `--path newton_schulz` measures the next row instead: Muon's Newton-Schulz
 orthogonalisation of whole expert matrices (one step = the gate, up and down
@@ -219,73 +221,117 @@ def bench_newton_schulz(args, torch, B):
     print(json.dumps(out), flush=True)
 
 
-BWD_METRIC = "MoE expert-FFN backward tokens/s + % bf16 MFMA peak (d6144,E384,top8)"
+BWD_METRIC = "MoE-layer backward tokens/s + expert-backward % bf16 MFMA peak (d6144,E384,top8)"
+
+
+class _ExpertBits:
+    """Per-expert bf16 weights as uint16 bit patterns on the host (the oracle
+    widens them to float64 one expert at a time)."""
+
+    def __init__(self, torch, t):
+        import numpy as np
+        self.h = t.cpu()
+        self.np, self.torch = np, torch
+
+    def __len__(self):
+        return self.h.shape[0]
+
+    def __getitem__(self, e):
+        return self.h[e].view(self.torch.int16).numpy().view(self.np.uint16)
 
 
 def bench_backward(args, torch, B, W):
-    """One step: moe_grouped_ffn_backward over every slot of the workload (token
-    rows read in place), dY random.  Algorithmic work 12 N d F (dH, dX, three
-    weight gradients); the kernels also recompute G and U (4 N d F more)."""
+    """One step: moe_layer_backward over the whole workload from the forward's
+    routing and expert outputs (computed once, beforehand, by the forward's own
+    entry points) and a seeded output gradient.  Algorithmic work of the expert
+    part 12 N d F (dH, dX, three weight gradients); its kernels also recompute G
+    and U (4 N d F more)."""
     import numpy as np
     wl = W.WORKLOADS[args.workload]
-    inp = W.make_inputs(wl, device="cuda:0")
-    if inp["w_router"] is not None:
-        ids, w, _ = B.moe_route(inp["x"], inp["w_router"], wl.k, bias=inp["bias"], want_logits=False)
+    dev = "cuda:0"
+    inp = W.make_inputs(wl, device=dev)
+    x, wr, wg, wu, wd = inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"]
+    if wr is not None:
+        ids, w, _ = B.moe_route(x, wr, wl.k, bias=inp["bias"], want_logits=False)
     else:
         ids, w = inp["topk_ids"], inp["topk_w"]
-    off, rt, sr, _ = B.moe_permute(inp["x"], ids, wl.E, copy_rows=False)
-    g = torch.Generator(device="cuda:0").manual_seed(1)
-    dy = torch.randn(rt.numel(), wl.d, generator=g, device="cuda:0").to(wl.dtype)
-    call = B.GroupedFfnBackward(inp["x"], off, inp["w_gate"], inp["w_up"], inp["w_down"], dy, a_rows=rt)
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        call()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    off, rt, sr, _ = B.moe_permute(x, ids, wl.E, copy_rows=False)
+    y_perm = B.moe_grouped_ffn(x, off, wg, wu, wd, a_rows=rt, n_max=rt.numel())
+    dy = W.output_grad(wl.T, wl.d, wl.dtype, dev, seed=1)
     n = int(off[-1])
+
+    def timed(fn, reps):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / reps
+
+    L = B.LayerBackward(x, wr, wg, wu, wd, ids, w, y_perm, dy)
+    for _ in range(args.warmup):
+        L()
+    torch.cuda.synchronize()
+    ms = timed(L, args.steps)
+    del L
+    torch.cuda.empty_cache()
+
+    # stage by stage, each on its own (same kernels as inside moe_layer_backward)
+    dy_perm = torch.empty(rt.numel(), wl.d, dtype=wl.dtype, device=dev)
+    stages = {}
+    stages["permute"] = timed(lambda: B.moe_permute(x, ids, wl.E, copy_rows=False), 2)
+    stages["combine_backward"] = timed(lambda: B.moe_combine_backward(dy, y_perm, sr, w, dy_perm=dy_perm), 2)
+    _, gw = B.moe_combine_backward(dy, y_perm, sr, w, dy_perm=dy_perm)
+    ffn = B.GroupedFfnBackward(x, off, wg, wu, wd, dy_perm, a_rows=rt)
+    ffn()
+    ffn_ms = timed(ffn, 2)
+    stages["grouped_ffn_backward"] = ffn_ms
+    dxp = ffn.dx
+    del ffn
+    torch.cuda.empty_cache()
+    if wr is not None:
+        stages["route_backward"] = timed(lambda: B.moe_route_backward(x, wr, ids, w, gw, dx_perm=dxp, slot_row=sr), 2)
     flops = 12 * n * wl.d * wl.F
-    tflops = flops / (ms / 1e3) / 1e12
+    tflops = flops / (ffn_ms / 1e3) / 1e12
     out = {
         "metric": BWD_METRIC, "value": round(wl.T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded random inputs, weights and output gradients of the page's layer shape)",
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded random inputs, weights and output gradient of the page's layer shape; routing "
+                "and expert outputs from the forward's entry points)",
         "config": {"workload": wl.name + "_backward", "tokens": wl.T, "hidden": wl.d, "experts": wl.E,
                    "top_k": wl.k, "expert_hidden": wl.F, "slots": n},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "moe_grouped_ffn_backward (7 GEMM launches, weight and activation transposes)",
-                     "flops_per_launch": flops, "ms_per_launch": round(ms, 4),
+                     "kernel": "grouped expert-FFN backward (7 GEMM launches, weight and activation transposes)",
+                     "flops_per_launch": flops, "ms_per_launch": round(ffn_ms, 4),
                      "note": "achieved counts 12 N d F; the G/U recompute (4 N d F) is extra work"},
+        "stages_ms": {k_: round(v, 4) for k_, v in stages.items()},
     }
     if args.cpu_tokens > 0:
         from threadpoolctl import threadpool_info
-        from oracle import moe_backward_oracle as bo
-        from oracle import moe_oracle as orc
+        from oracle import moe_layer_backward_oracle as lbo
         nt = min(args.cpu_tokens, wl.T)
-        ids_h = ids[:nt].cpu().numpy().astype(np.int64)
-        off_h, rt_h, _ = orc.permute(ids_h, wl.E)
-        X = inp["x"][:nt].float().cpu().numpy().astype(np.float64)[rt_h]
-        dY = np.random.default_rng(2).standard_normal((len(rt_h), wl.d))
+        ids_h = ids[:nt].cpu().numpy()
+        w_h = w[:nt].cpu().numpy()
         f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
-        used = [e for e in range(wl.E) if off_h[e + 1] > off_h[e]]
-        wg = {e: f64(inp["w_gate"][e]) for e in used}
-        wu = {e: f64(inp["w_up"][e]) for e in used}
-        wd = {e: f64(inp["w_down"][e]) for e in used}
+        slots = int((ids_h >= 0).sum())
+        rng = np.random.default_rng(2)
+        yp = rng.standard_normal((slots, wl.d))
+        dyh = rng.standard_normal((nt, wl.d))
+        Xh = f64(x[:nt])
+        Wr = f64(wr) if wr is not None else None
+        ew = [_ExpertBits(torch, t) for t in (wg, wu, wd)]
         t0 = time.perf_counter()
-        for e in used:
-            lo, hi = off_h[e], off_h[e + 1]
-            bo.expert_ffn_backward(X[lo:hi], wg[e], wu[e], wd[e], dY[lo:hi])
+        lbo.layer_backward(Xh, Wr, ew[0], ew[1], ew[2], ids_h, w_h, yp, dyh)
         dt = time.perf_counter() - t0
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        used = len(np.unique(ids_h[ids_h >= 0]))
         out["cpu_baseline"] = {"value": round(nt / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-                               "sample": f"first {nt} of {wl.T} tokens ({len(rt_h)} slots, {len(used)} experts): "
-                                         f"float64 expert backward {dt:.1f} s on {threads} BLAS threads"}
+                               "sample": f"first {nt} of {wl.T} tokens ({slots} slots, {used} experts): float64 "
+                                         f"layer backward (combine, expert, gate-weight/router and permutation "
+                                         f"backward) {dt:.1f} s on {threads} BLAS threads"}
     print(json.dumps(out), flush=True)
 
 
