@@ -21,9 +21,9 @@
 //   * the weight gradients contract over each expert's rows: the activations
 //     are transposed into a layout where expert e owns columns
 //     [poff[e], poff[e+1]) (its row count rounded up to 64, the gap zero-filled),
-//     and one GEMM per gradient runs with one group per expert whose k range
-//     is that column range, every group reading the same operand rows.  An
-//     expert with no rows gets a zero gradient.
+//     stored k-blocked (below), and one GEMM per gradient runs with one group per
+//     expert whose k range is that column range, every group reading the same
+//     operand rows.  An expert with no rows gets a zero gradient.
 #include "common.h"
 #include "gemm_tile.h"
 #include "kernels.h"
@@ -33,6 +33,17 @@ namespace moe {
 namespace {
 
 constexpr int kTile = 64;
+
+// Tile order of the weight-gradient GEMMs inside an expert (see GemmArgs): row
+// tiles in chunks of kWgradRowChunk, column tiles in groups of kWgradColumnGroup,
+// so the 32 tiles an XCD runs side by side form a 4 x 8 block and share their A
+// rows and B rows in that XCD's L2 (all row or all column tiles of an expert would
+// stream one of the two operands once per XCD that holds part of the expert).
+constexpr int kWgradRowChunk = 4;
+constexpr int kWgradColumnGroup = 8;
+// The same for the GEMMs over the expert rows (dH, recompute, dX); 0: not chunked.
+constexpr int kRowsRowChunk = 0;
+constexpr int kRowsColumnGroup = 0;
 
 // poff[e] = sum over e' < e of the row count of e' rounded up to 64 (one block).
 __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __restrict__ offsets, int E,
@@ -55,25 +66,28 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __rest
   if (e == E - 1) poff[E] = before + incl;
 }
 
-// dst[c, p] (row stride ld_dst) for padded column p of expert e = src row
-// offsets[e] + (p - poff[e]) (through rows[] when given), columns col0 + c of the
-// source (row stride ld_src); zero past the expert's rows.  One 64 x 64 tile per
-// block; blocks past poff[E] have nothing to do.
-template <typename T>
+// The transposed, padded activations are stored k-blocked: element (c, p) of an
+// [R, n_pad] matrix (c < R a feature, p a padded row) sits at
+// (p / KW) R KW + c KW + p % KW, i.e. every KW-wide column block is one contiguous
+// [R, KW] piece.  A weight-gradient tile then reads each k-step (256 features x KW
+// rows) as one contiguous 32 KB piece, where a plain [R, n_pad] layout would touch
+// 256 rows a megabyte apart (one address-translation page each).
+//
+// Element (c, p) for padded row p of expert e = source row offsets[e] + (p - poff[e])
+// (through rows[] when given), column col0 + c of the source (row stride ld_src);
+// zero past the expert's rows.  One 64 x 64 tile per block; blocks past poff[E] have
+// nothing to do; pblk_expert[p / 64] is the expert owning padded rows p .. p + 63.
+template <typename T, int KW>
 __global__ __launch_bounds__(256) void pad_transpose_kernel(const T* __restrict__ src, int64_t ld_src, int col0,
                                                             const int32_t* __restrict__ rows,
                                                             const int32_t* __restrict__ offsets,
-                                                            const int32_t* __restrict__ poff, int E,
-                                                            T* __restrict__ dst, int64_t ld_dst) {
+                                                            const int32_t* __restrict__ poff,
+                                                            const int32_t* __restrict__ pblk_expert, int E,
+                                                            T* __restrict__ dst, int64_t R) {
   __shared__ T tile[kTile][kTile + 2];
   const int p0 = blockIdx.x * kTile;
   if (p0 >= poff[E]) return;
-  int lo = 0, hi = E;                       // largest e with poff[e] <= p0
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (poff[mid] <= p0) lo = mid; else hi = mid;
-  }
-  const int e = lo;
+  const int e = pblk_expert[blockIdx.x];
   const int r0 = p0 - poff[e];
   const int n_e = offsets[e + 1] - offsets[e];
   const int c0 = blockIdx.y * kTile;
@@ -88,7 +102,24 @@ __global__ __launch_bounds__(256) void pad_transpose_kernel(const T* __restrict_
     tile[j][tx] = v;
   }
   __syncthreads();
-  for (int i = ty; i < kTile; i += 4) dst[(int64_t)(c0 + i) * ld_dst + p0 + tx] = tile[tx][i];
+  const int p = p0 + tx;
+  T* out = dst + (int64_t)(p / KW) * R * KW + p % KW;
+  for (int i = ty; i < kTile; i += 4) out[(int64_t)(c0 + i) * KW] = tile[tx][i];
+}
+
+// pblk_expert[b] = the expert owning padded rows 64 b .. 64 b + 63 (largest e with
+// poff[e] <= 64 b), for every block b below poff[E] / 64.
+__global__ __launch_bounds__(256) void pad_block_experts_kernel(const int32_t* __restrict__ poff, int E,
+                                                                int32_t* __restrict__ pblk_expert) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  const int p0 = b * kTile;
+  if (p0 >= poff[E]) return;
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (poff[mid] <= p0) lo = mid; else hi = mid;
+  }
+  pblk_expert[b] = lo;
 }
 
 // dst[b][c * ld_dst + coff + r] = src[b][r * cols + c] for b < batch: transposes
@@ -125,7 +156,11 @@ GemmArgs args_grouped(const void* A, const int32_t* a_rows, const void* B0, cons
 }
 
 template <typename T, int BK, int EPI, int FEAT = 0>
-void gemm(const GemmArgs& a, int num_cu, hipStream_t s) {
+void gemm(GemmArgs a, int num_cu, hipStream_t s) {
+  if (a.m_chunk == 0 && a.n_group == 0) {
+    a.m_chunk = (FEAT & kFeatStrides) ? kWgradRowChunk : kRowsRowChunk;
+    a.n_group = (FEAT & kFeatStrides) ? kWgradColumnGroup : kRowsColumnGroup;
+  }
   hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, 4, 2, 2, EPI, 1, FEAT>), dim3(num_cu), dim3(512), 0, s, a);
 }
 
@@ -163,26 +198,32 @@ hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const 
                              (int)(2 * F), dx_perm);
   gemm<T, BK, EPI_STORE>(a3, num_cu, s);
 
-  // transposed, padded activations for the weight gradients
-  const dim3 gd((unsigned)(np / kTile), (unsigned)(d / kTile)), gf((unsigned)(np / kTile), (unsigned)(F / kTile));
-  hipLaunchKernelGGL((pad_transpose_kernel<T>), gd, dim3(256), 0, s, static_cast<const T*>(x_in), d, 0, a_rows,
-                     offsets, w.poff, (int)E, static_cast<T*>(w.x_t), np);
-  hipLaunchKernelGGL((pad_transpose_kernel<T>), gd, dim3(256), 0, s, static_cast<const T*>(dy_perm), d, 0,
-                     (const int32_t*)nullptr, offsets, w.poff, (int)E, static_cast<T*>(w.dy_t), np);
-  hipLaunchKernelGGL((pad_transpose_kernel<T>), gf, dim3(256), 0, s, static_cast<const T*>(w.h), F, 0,
-                     (const int32_t*)nullptr, offsets, w.poff, (int)E, static_cast<T*>(w.h_t), np);
-  hipLaunchKernelGGL((pad_transpose_kernel<T>), gf, dim3(256), 0, s, static_cast<const T*>(w.dgu), 2 * F, 0,
-                     (const int32_t*)nullptr, offsets, w.poff, (int)E, static_cast<T*>(w.dg_t), np);
-  hipLaunchKernelGGL((pad_transpose_kernel<T>), gf, dim3(256), 0, s, static_cast<const T*>(w.dgu), 2 * F, (int)F,
-                     (const int32_t*)nullptr, offsets, w.poff, (int)E, static_cast<T*>(w.du_t), np);
+  // transposed, padded, k-blocked activations for the weight gradients
+  const unsigned nblk = (unsigned)(np / kTile);
+  hipLaunchKernelGGL(pad_block_experts_kernel, dim3((nblk + 255) / 256), dim3(256), 0, s, w.poff, (int)E,
+                     w.pblk_expert);
+  const dim3 gd(nblk, (unsigned)(d / kTile)), gf(nblk, (unsigned)(F / kTile));
+  hipLaunchKernelGGL((pad_transpose_kernel<T, BK>), gd, dim3(256), 0, s, static_cast<const T*>(x_in), d, 0, a_rows,
+                     offsets, w.poff, w.pblk_expert, (int)E, static_cast<T*>(w.x_t), d);
+  hipLaunchKernelGGL((pad_transpose_kernel<T, BK>), gd, dim3(256), 0, s, static_cast<const T*>(dy_perm), d, 0,
+                     (const int32_t*)nullptr, offsets, w.poff, w.pblk_expert, (int)E, static_cast<T*>(w.dy_t), d);
+  hipLaunchKernelGGL((pad_transpose_kernel<T, BK>), gf, dim3(256), 0, s, static_cast<const T*>(w.h), F, 0,
+                     (const int32_t*)nullptr, offsets, w.poff, w.pblk_expert, (int)E, static_cast<T*>(w.h_t), F);
+  hipLaunchKernelGGL((pad_transpose_kernel<T, BK>), gf, dim3(256), 0, s, static_cast<const T*>(w.dgu), 2 * F, 0,
+                     (const int32_t*)nullptr, offsets, w.poff, w.pblk_expert, (int)E, static_cast<T*>(w.dg_t), F);
+  hipLaunchKernelGGL((pad_transpose_kernel<T, BK>), gf, dim3(256), 0, s, static_cast<const T*>(w.dgu), 2 * F,
+                     (int)F, (const int32_t*)nullptr, offsets, w.poff, w.pblk_expert, (int)E,
+                     static_cast<T*>(w.du_t), F);
 
   // weight gradients: one group per expert, k over its padded column range
   auto wgrad = [&](const void* A, int rows, const void* B, int N, float* C) {
     GemmArgs a = args_grouped(A, nullptr, B, nullptr, 0, nullptr, (int)E, E * rows, N, 0, C);
     a.group_rows = rows;
     a.a_shared = 1;
-    a.lda = np;
-    a.ldb = np;
+    a.lda = BK;
+    a.ldb = BK;
+    a.ksa = (int64_t)rows * BK;
+    a.ksb = (int64_t)N * BK;
     a.kseg = w.poff;
     gemm<T, BK, EPI_F32_BIAS, kFeatGroups | kFeatStrides>(a, num_cu, s);
   };

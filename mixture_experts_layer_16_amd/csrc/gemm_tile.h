@@ -78,6 +78,10 @@ struct GemmArgs {
                           // tile block is A row r, not the group's first row + r)
   void* C2;               // EPI_SWIGLU_BWD: H = silu(G) * U, [rows, N]
   int64_t ldc;            // row stride of C in elements (0: N)
+  int64_t ksa, ksb;       // elements from one BK-deep k-slice of A (B) to the next
+                          // (0: BK).  With lda = BK and ksa = rows * BK, A is stored
+                          // k-blocked: slice j is a contiguous [rows, BK] block, so a
+                          // tile's k-step reads one contiguous piece of memory
 };
 
 // Per element type: how one wave multiplies a 32x32 block over 16 k values.
@@ -250,7 +254,7 @@ __device__ void build_tile_prefix(const int32_t* seg, int G, int64_t M, int64_t 
 // PD: how many 16-k sub-steps ahead the MFMA operand fragments are read from LDS
 // FEAT (compile-time, so that kernels without them compile as if absent):
 //   kFeatGroups:  equal groups without offsets (seg == nullptr, group_rows > 0);
-//   kFeatStrides: lda, ldb, kseg and a_shared;
+//   kFeatStrides: lda, ldb, ksa, ksb, kseg and a_shared;
 // otherwise those fields are ignored: operands are [rows, K] with one K for every
 // group, and the groups come from seg (or are one group of M rows).
 template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, int PD = 1, int FEAT = 0>
@@ -357,12 +361,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   uint32_t soff[CPT];
   auto setup = [&](const TileInfo& t, const int* arow) {
     const int64_t k0 = STR ? t.k0 : 0;
-    Ab = reinterpret_cast<const char*>(Abase + k0 + (p.a_rows ? 0 : ((STR && p.a_shared) ? t.mrel : t.m0) * lda));
+    const int64_t ka0 = (STR && p.ksa) ? k0 / BK * p.ksa : k0, kb0 = (STR && p.ksb) ? k0 / BK * p.ksb : k0;
+    Ab = reinterpret_cast<const char*>(Abase + ka0 + (p.a_rows ? 0 : ((STR && p.a_shared) ? t.mrel : t.m0) * lda));
     Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)t.g * p.b_stride + (int64_t)t.n0 * ldb +
-                                        k0);
+                                        kb0);
     if (paired_epilogue(EPI))
       Bub = reinterpret_cast<const char*>(static_cast<const T*>(p.B1) + (int64_t)t.g * p.b_stride +
-                                          (int64_t)t.n0 * ldb + k0);
+                                          (int64_t)t.n0 * ldb + kb0);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       // whether load step i reads A, gate or up is known at compile time
@@ -384,8 +389,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   // copy i (of CPT) of k-tile kt into `stage`
   auto load_one = [&](int stage, int kt, int i) {
     const uint32_t lbase = lds_addr_of(smem) + stage * Cfg::kStageBytes + wave * 64 * 16;
-    const int64_t kb = (int64_t)kt * BK * (int64_t)sizeof(T);
     const int row0 = i * Cfg::kRowsPerStep;
+    int64_t kstep = BK;
+    if constexpr (STR) {
+      const int64_t ks = row0 < BM ? p.ksa : p.ksb;
+      if (ks) kstep = ks;
+    }
+    const int64_t kb = (int64_t)kt * kstep * (int64_t)sizeof(T);
     const char* base;
     if (row0 < BM) base = Ab;
     else if (paired_epilogue(EPI) && row0 - BM >= BN / 2) base = Bub;

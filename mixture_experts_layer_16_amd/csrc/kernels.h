@@ -44,16 +44,18 @@ hipError_t launch_newton_schulz(int64_t n, int64_t R, int64_t C, int64_t steps, 
 // from dy_perm.  Scratch (caller-carved; "I/O" = the dtype's element type):
 struct FfnBackwardScratch {
   int32_t* poff;   // [E+1] padded expert column offsets
+  int32_t* pblk_expert;  // [n_pad / 64] expert of each 64-wide padded column block
   void* wd_t;      // [E, F, d]   W_d transposed (I/O)
   void* wgu_t;     // [E, d, 2F]  W_g and W_u transposed, side by side (I/O)
   float* dh;       // [n_max, F]  dH (float32)
   void* dgu;       // [n_max, 2F] dG | dU (I/O)
   void* h;         // [n_max, F]  H recomputed (I/O)
-  void* x_t;       // [d, n_pad]  expert rows of the input, transposed and padded (I/O)
-  void* dy_t;      // [d, n_pad]  (I/O)
-  void* h_t;       // [F, n_pad]  (I/O)
-  void* dg_t;      // [F, n_pad]  (I/O)
-  void* du_t;      // [F, n_pad]  (I/O)
+  void* x_t;       // [d, n_pad]  expert rows of the input, transposed and padded, stored
+                   //             k-blocked ([n_pad / BK] blocks of [d, BK]) (I/O)
+  void* dy_t;      // [d, n_pad]  k-blocked (I/O)
+  void* h_t;       // [F, n_pad]  k-blocked (I/O)
+  void* dg_t;      // [F, n_pad]  k-blocked (I/O)
+  void* du_t;      // [F, n_pad]  k-blocked (I/O)
   int64_t n_pad;   // >= sum over experts of rows rounded up to 64; a multiple of 64
 };
 hipError_t launch_grouped_ffn_backward(int dtype, int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_in,
@@ -79,8 +81,8 @@ hipError_t launch_combine_backward(int dtype, int64_t T, int64_t d, int64_t k, c
 constexpr int kMaxSplits = 16;
 struct RouteBackwardScratch {
   float* dlogits;        // [T, E] dense logit gradient
-  void* dl_t;            // [E, t_pad] its transpose (I/O type)
-  void* x_t;             // [d, t_pad] x transposed (I/O type)
+  void* dl_t;            // [E, t_pad] its transpose, k-blocked (I/O type)
+  void* x_t;             // [d, t_pad] x transposed, k-blocked (I/O type)
   int32_t* kseg;         // [splits + 1] token ranges of the split GEMM
   float* split_partial;  // [splits, E, d] when splits > 1
   float* bias_partial;   // [bias_chunks, E]

@@ -17,8 +17,9 @@
 //       db[e] = sum_t dl[t,e]           (float32 column sums, two fixed-order passes),
 //       dW_r = dl^T x                   (MFMA: dl and x transposed to [E, T'] and
 //                                        [d, T'], T' = T rounded up to 64 with zero
-//                                        columns; one NT GEMM split over k ranges of
-//                                        tokens, the float32 partials summed in order).
+//                                        columns, stored k-blocked; one NT GEMM split
+//                                        over k ranges of tokens, the float32 partials
+//                                        summed in order).
 #include <algorithm>
 
 #include "common.h"
@@ -222,13 +223,15 @@ __global__ __launch_bounds__(256) void column_sum_final_kernel(const float* __re
   out[e] = s;
 }
 
-// dst[c * ld_dst + r] = src[r * cols + c] for r < rows, 0 for rows <= r < ld_dst;
-// c < cols.  One 64 x 64 tile per block (grid: ceil(cols/64) x ld_dst/64), values
-// passed through float32 (exact for bf16 -> bf16 and float -> float; float -> bf16
-// rounds to nearest even).
-template <typename Ts, typename Td>
+// Transpose with zero padding, stored k-blocked: element (c, r) of the [cols, T']
+// result (c < cols, r < T' = gridDim.y * 64) is src[r * cols + c] for r < rows and
+// 0 beyond, at (r / KW) cols KW + c KW + r % KW (every KW-wide block of r is one
+// contiguous [cols, KW] piece, which a GEMM k-step reads whole).  One 64 x 64 tile
+// per block; values pass through float32 (exact for bf16 -> bf16 and float ->
+// float; float -> bf16 rounds to nearest even).
+template <typename Ts, typename Td, int KW>
 __global__ __launch_bounds__(256) void transpose_pad_kernel(const Ts* __restrict__ src, int rows, int cols,
-                                                            Td* __restrict__ dst, int64_t ld_dst) {
+                                                            Td* __restrict__ dst) {
   __shared__ float tile[kTile][kTile + 1];
   const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -237,9 +240,11 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const Ts* __restrict
     tile[i][tx] = (r < rows && c < cols) ? to_f32(src[(int64_t)r * cols + c]) : 0.f;
   }
   __syncthreads();
+  const int r = r0 + tx;
+  Td* out = dst + (int64_t)(r / KW) * cols * KW + r % KW;
   for (int i = ty; i < kTile; i += 4) {
     const int c = c0 + i;
-    if (c < cols) dst[(int64_t)c * ld_dst + r0 + tx] = from_f32<Td>(tile[tx][i]);
+    if (c < cols) out[(int64_t)c * KW] = from_f32<Td>(tile[tx][i]);
   }
 }
 
@@ -321,10 +326,10 @@ hipError_t route_backward_t(int64_t T_, int64_t d, int64_t E, int64_t k, const T
   // dW_r = dl^T x on the transposed, zero-padded operands
   T* dlt = static_cast<T*>(ws.dl_t);
   T* xt = static_cast<T*>(ws.x_t);
-  hipLaunchKernelGGL((transpose_pad_kernel<float, T>), dim3((unsigned)((E + 63) / 64), (unsigned)(tp / kTile)),
-                     dim3(256), 0, s, ws.dlogits, (int)T_, (int)E, dlt, tp);
-  hipLaunchKernelGGL((transpose_pad_kernel<T, T>), dim3((unsigned)(d / kTile), (unsigned)(tp / kTile)), dim3(256), 0,
-                     s, x, (int)T_, (int)d, xt, tp);
+  hipLaunchKernelGGL((transpose_pad_kernel<float, T, BK>), dim3((unsigned)((E + 63) / 64), (unsigned)(tp / kTile)),
+                     dim3(256), 0, s, ws.dlogits, (int)T_, (int)E, dlt);
+  hipLaunchKernelGGL((transpose_pad_kernel<T, T, BK>), dim3((unsigned)(d / kTile), (unsigned)(tp / kTile)),
+                     dim3(256), 0, s, x, (int)T_, (int)d, xt);
   hipLaunchKernelGGL(split_offsets_kernel, dim3(1), dim3(64), 0, s, ws.kseg, ws.splits, (int)(tp / BK), BK);
   GemmArgs a{};
   a.A = dlt;
@@ -337,8 +342,10 @@ hipError_t route_backward_t(int64_t T_, int64_t d, int64_t E, int64_t k, const T
   a.K = 0;
   a.C = ws.splits > 1 ? static_cast<void*>(ws.split_partial) : static_cast<void*>(dw_router);
   a.a_shared = 1;
-  a.lda = tp;
-  a.ldb = tp;
+  a.lda = BK;
+  a.ldb = BK;
+  a.ksa = E * BK;
+  a.ksb = d * BK;
   a.kseg = ws.kseg;
   hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, 4, 2, 2, EPI_F32_BIAS, 1, kFeatGroups | kFeatStrides>),
                      dim3(num_cu), dim3(512), 0, s, a);

@@ -112,6 +112,7 @@ void carve_ffn_backward(Carver& c, moe::FfnBackwardScratch& w, int64_t n_max, in
                         size_t es) {
   const int64_t n_pad = (n_max + 63 * E + 63) / 64 * 64;
   w.poff = static_cast<int32_t*>(c.take((size_t)(E + 1) * 4));
+  w.pblk_expert = static_cast<int32_t*>(c.take((size_t)(n_pad / 64) * 4));
   w.wd_t = c.take((size_t)E * F * d * es);
   w.wgu_t = c.take((size_t)E * d * 2 * F * es);
   w.dh = static_cast<float*>(c.take((size_t)n_max * F * 4));
