@@ -39,6 +39,8 @@ template <int N, int I = 0, typename F> __device__ __forceinline__ void static_f
   }
 }
 
+template <typename X> struct TypeTag { typedef X type; };
+
 constexpr int kMaxGroups = 1024;
 constexpr int kXcds = 8;   // accelerator complex dies of an MI355X, one L2 each
 // A recycled stage's copies are threaded between the MFMAs of the kDmaSpread
@@ -480,33 +482,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     const int en0 = t.n0, erows = t.rows_valid;
 
     const int h4 = 4 * (lane >> 5);
-    if constexpr (EPI == EPI_F32_BIAS) {
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int r = wm * Cfg::WTM + mi * 32 + (lane & 31);
-        if (r >= erows) continue;
-        float* crow = static_cast<float*>(p.C) + (em0 + r) * (int64_t)p.N;
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int col = en0 + wn * Cfg::WTN + ni * 32 + 8 * q + h4;
-            if ((p.N & 3) == 0) {
-              if (col < p.N) {
-                f32x4 v;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = acc[mi][ni][4 * q + i] + (p.bias ? p.bias[col + i] : 0.f);
-                *reinterpret_cast<f32x4*>(crow + col) = v;
-              }
-            } else {
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (col + i < p.N) crow[col + i] = acc[mi][ni][4 * q + i] + (p.bias ? p.bias[col + i] : 0.f);
-            }
-          }
-      }
-    } else if constexpr (EPI != EPI_AXPBY && EPI != EPI_SWIGLU_BWD && NT == 512 && Cfg::WTM == 64 &&
-                         8 * kEpiWaveBytes <= Cfg::kStageBytes) {
+    // Staged through LDS, for an output element type OT (T, or float for
+    // EPI_F32_BIAS).
+    auto staged = [&](auto ot_tag) {
+      typedef typename decltype(ot_tag)::type OT;
       // Staged through LDS (wbuf: this wave's 32 rows x 144 bytes, which nothing
       // else touches until the next barrier).  Per round
       // (one row block mi, 128 bytes of output columns) it parks its values there
@@ -515,7 +494,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
       // row, and stores whole 128-byte row segments.
       constexpr int NO = paired_epilogue(EPI) ? NI / 2 : NI;
       constexpr int CW = paired_epilogue(EPI) ? Cfg::WTN / 2 : Cfg::WTN;   // output columns per wave
-      constexpr int ES = (int)sizeof(T);
+      constexpr int ES = (int)sizeof(OT);
       constexpr int RC = 128 / ES;                                         // columns per round
       constexpr int ROUNDS = CW / RC;
       constexpr int RS = kEpiRowBytes;
@@ -527,7 +506,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
       const int r0 = wm * Cfg::WTM + (lane >> 3);
       const int rrem = erows - r0;
       const int c0l = en0 + wn * CW + (lane & 7) * (16 / ES);
-      T* cbase = static_cast<T*>(p.C) + (em0 + r0) * (int64_t)p.N + c0l;
+      OT* cbase = static_cast<OT*>(p.C) + (em0 + r0) * (int64_t)p.N + c0l;
       const int64_t rstep = 8 * (int64_t)p.N;
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
@@ -547,22 +526,46 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
                   const float gv = acc[mi][ni][4 * q + i];
                   const float uv = acc[mi][ni + NI / 2][4 * q + i];
                   v[i] = gv / (1.0f + __expf(-gv)) * uv;
+                } else if constexpr (EPI == EPI_F32_BIAS) {
+                  const int col = en0 + wn * CW + ni * 32 + 8 * q + h4;
+                  v[i] = acc[mi][ni][4 * q + i] + ((p.bias && col + i < p.N) ? p.bias[col + i] : 0.f);
                 } else {
                   v[i] = acc[mi][ni][4 * q + i];
                 }
               }
-              store4(reinterpret_cast<T*>(wlane + c0 * ES), v);
+              store4(reinterpret_cast<OT*>(wlane + c0 * ES), v);
             }
           wait_lgkmcnt0();
 #pragma unroll
           for (int it = 0; it < 4; ++it) {
             const u32x4 val = *reinterpret_cast<const u32x4*>(rlane + it * 8 * RS);
-            if (mi * 32 + it * 8 < rrem && c0l + rd * RC < p.N)
-              *reinterpret_cast<u32x4*>(cbase + (4 * mi + it) * rstep + rd * RC) = val;
+            const int cc = c0l + rd * RC;
+            if constexpr (EPI == EPI_F32_BIAS) {
+              // N need not be a multiple of 4 here (a router's expert count)
+              if (mi * 32 + it * 8 < rrem) {
+                OT* dst = cbase + (4 * mi + it) * rstep + rd * RC;
+                if (cc + 16 / ES <= p.N) {
+                  *reinterpret_cast<u32x4*>(dst) = val;
+                } else if (cc < p.N) {
+                  const OT* ev = reinterpret_cast<const OT*>(&val);
+                  for (int i = 0; i < 16 / ES && cc + i < p.N; ++i) dst[i] = ev[i];
+                }
+              }
+            } else {
+              if (mi * 32 + it * 8 < rrem && cc < p.N)
+                *reinterpret_cast<u32x4*>(cbase + (4 * mi + it) * rstep + rd * RC) = val;
+            }
           }
           wait_lgkmcnt0();
         }
       }
+    };
+    constexpr bool kStaged = EPI != EPI_AXPBY && EPI != EPI_SWIGLU_BWD && NT == 512 && Cfg::WTM == 64 &&
+                             8 * kEpiWaveBytes <= Cfg::kStageBytes;
+    if constexpr (kStaged) {
+      staged(TypeTag<typename std::conditional<EPI == EPI_F32_BIAS, float, T>::type>{});
+    } else if constexpr (EPI == EPI_F32_BIAS) {
+      static_assert(EPI != EPI_F32_BIAS, "float32 outputs take the staged epilogue");
     } else {
       constexpr int NO = paired_epilogue(EPI) ? NI / 2 : NI;
       constexpr int CW = paired_epilogue(EPI) ? Cfg::WTN / 2 : Cfg::WTN;
