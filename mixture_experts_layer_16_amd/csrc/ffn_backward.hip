@@ -27,6 +27,7 @@
 #include "common.h"
 #include "gemm_tile.h"
 #include "kernels.h"
+#include "transpose.h"
 
 namespace moe {
 
@@ -122,6 +123,47 @@ __global__ __launch_bounds__(256) void pad_block_experts_kernel(const int32_t* _
   pblk_expert[b] = lo;
 }
 
+// 16-bit elements: the same result as pad_transpose_kernel with KW = 64, in strips
+// of up to 8 tiles (grid.y walks the strips of the R source columns).
+__global__ __launch_bounds__(256) void pad_transpose16_kernel(const uint16_t* __restrict__ src, int64_t ld_src,
+                                                              int col0, const int32_t* __restrict__ rows,
+                                                              const int32_t* __restrict__ offsets,
+                                                              const int32_t* __restrict__ poff,
+                                                              const int32_t* __restrict__ pblk_expert, int E,
+                                                              uint16_t* __restrict__ dst, int64_t R) {
+  const int p0 = blockIdx.x * kTile;
+  if (p0 >= poff[E]) return;
+  const int e = pblk_expert[blockIdx.x];
+  const int r0 = p0 - poff[e];
+  const int n_e = offsets[e + 1] - offsets[e];
+  const int cs = blockIdx.y * 8 * kTile;                         // first source column of the strip
+  const int ntile = min(8, (int)(R / kTile) - blockIdx.y * 8);
+  uint16_t* blk = dst + (int64_t)(p0 / kTile) * R * kTile;
+  transpose_strip16(
+      ntile,
+      [&](int r) -> const uint16_t* {
+        if (r0 + r >= n_e) return nullptr;
+        const int64_t sr = offsets[e] + r0 + r;
+        const int64_t row = rows ? (int64_t)rows[sr] : sr;
+        return src + row * ld_src + col0 + cs;
+      },
+      [&](int j, int c) { return blk + (int64_t)(cs + j * kTile + c) * kTile; });
+}
+
+// 16-bit elements: transpose_into_kernel in strips of up to 8 tiles along the
+// source columns (grid: strips x rows / 64 x batch).
+__global__ __launch_bounds__(256) void transpose_into16_kernel(const uint16_t* __restrict__ src, int rows, int cols,
+                                                               uint16_t* __restrict__ dst, int64_t ld_dst, int coff,
+                                                               int64_t dst_batch) {
+  const uint16_t* S = src + (int64_t)blockIdx.z * rows * cols;
+  uint16_t* D = dst + (int64_t)blockIdx.z * dst_batch;
+  const int r0 = blockIdx.y * kTile, cs = blockIdx.x * 8 * kTile;
+  const int ntile = min(8, cols / kTile - (int)blockIdx.x * 8);
+  transpose_strip16(
+      ntile, [&](int r) { return S + (int64_t)(r0 + r) * cols + cs; },
+      [&](int j, int c) { return D + (int64_t)(cs + j * kTile + c) * ld_dst + coff + r0; });
+}
+
 // dst[b][c * ld_dst + coff + r] = src[b][r * cols + c] for b < batch: transposes
 // of [rows, cols] matrices into column range [coff, coff + rows) of [cols, ld_dst].
 template <typename T>
@@ -176,12 +218,21 @@ hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const 
 
   // padded expert column ranges; transposed weights
   hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(1024), 0, s, offsets, (int)E, w.poff);
-  hipLaunchKernelGGL((transpose_into_kernel<T>), dim3((unsigned)(F / kTile), (unsigned)(d / kTile), (unsigned)E),
-                     dim3(256), 0, s, Wd, (int)d, (int)F, static_cast<T*>(w.wd_t), d, 0, F * d);
-  hipLaunchKernelGGL((transpose_into_kernel<T>), dim3((unsigned)(d / kTile), (unsigned)(F / kTile), (unsigned)E),
-                     dim3(256), 0, s, Wg, (int)F, (int)d, static_cast<T*>(w.wgu_t), 2 * F, 0, d * 2 * F);
-  hipLaunchKernelGGL((transpose_into_kernel<T>), dim3((unsigned)(d / kTile), (unsigned)(F / kTile), (unsigned)E),
-                     dim3(256), 0, s, Wu, (int)F, (int)d, static_cast<T*>(w.wgu_t), 2 * F, (int)F, d * 2 * F);
+  auto transpose_into = [&](const T* src, int rows, int cols, T* dst, int64_t ld_dst, int coff, int64_t batch) {
+    if constexpr (sizeof(T) == 2) {
+      const unsigned strips = (unsigned)((cols / kTile + 7) / 8);
+      hipLaunchKernelGGL(transpose_into16_kernel, dim3(strips, (unsigned)(rows / kTile), (unsigned)E), dim3(256), 0,
+                         s, reinterpret_cast<const uint16_t*>(src), rows, cols, reinterpret_cast<uint16_t*>(dst),
+                         ld_dst, coff, batch);
+    } else {
+      hipLaunchKernelGGL((transpose_into_kernel<T>), dim3((unsigned)(cols / kTile), (unsigned)(rows / kTile),
+                                                          (unsigned)E),
+                         dim3(256), 0, s, src, rows, cols, dst, ld_dst, coff, batch);
+    }
+  };
+  transpose_into(Wd, (int)d, (int)F, static_cast<T*>(w.wd_t), d, 0, F * d);
+  transpose_into(Wg, (int)F, (int)d, static_cast<T*>(w.wgu_t), 2 * F, 0, d * 2 * F);
+  transpose_into(Wu, (int)F, (int)d, static_cast<T*>(w.wgu_t), 2 * F, (int)F, d * 2 * F);
 
   // dH = dY W_d (float32)
   GemmArgs a1 = args_grouped(dy_perm, nullptr, w.wd_t, nullptr, F * d, offsets, (int)E, n_max, (int)F, (int)d,
@@ -202,18 +253,22 @@ hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const 
   const unsigned nblk = (unsigned)(np / kTile);
   hipLaunchKernelGGL(pad_block_experts_kernel, dim3((nblk + 255) / 256), dim3(256), 0, s, w.poff, (int)E,
                      w.pblk_expert);
-  const dim3 gd(nblk, (unsigned)(d / kTile)), gf(nblk, (unsigned)(F / kTile));
-  hipLaunchKernelGGL((pad_transpose_kernel<T, BK>), gd, dim3(256), 0, s, static_cast<const T*>(x_in), d, 0, a_rows,
-                     offsets, w.poff, w.pblk_expert, (int)E, static_cast<T*>(w.x_t), d);
-  hipLaunchKernelGGL((pad_transpose_kernel<T, BK>), gd, dim3(256), 0, s, static_cast<const T*>(dy_perm), d, 0,
-                     (const int32_t*)nullptr, offsets, w.poff, w.pblk_expert, (int)E, static_cast<T*>(w.dy_t), d);
-  hipLaunchKernelGGL((pad_transpose_kernel<T, BK>), gf, dim3(256), 0, s, static_cast<const T*>(w.h), F, 0,
-                     (const int32_t*)nullptr, offsets, w.poff, w.pblk_expert, (int)E, static_cast<T*>(w.h_t), F);
-  hipLaunchKernelGGL((pad_transpose_kernel<T, BK>), gf, dim3(256), 0, s, static_cast<const T*>(w.dgu), 2 * F, 0,
-                     (const int32_t*)nullptr, offsets, w.poff, w.pblk_expert, (int)E, static_cast<T*>(w.dg_t), F);
-  hipLaunchKernelGGL((pad_transpose_kernel<T, BK>), gf, dim3(256), 0, s, static_cast<const T*>(w.dgu), 2 * F,
-                     (int)F, (const int32_t*)nullptr, offsets, w.poff, w.pblk_expert, (int)E,
-                     static_cast<T*>(w.du_t), F);
+  auto pad_transpose = [&](const void* src, int64_t ld_src, int col0, const int32_t* rows, void* dst, int64_t R) {
+    if constexpr (sizeof(T) == 2 && BK == kTile) {
+      hipLaunchKernelGGL(pad_transpose16_kernel, dim3(nblk, (unsigned)((R / kTile + 7) / 8)), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(src), ld_src, col0, rows, offsets, w.poff, w.pblk_expert,
+                         (int)E, static_cast<uint16_t*>(dst), R);
+    } else {
+      hipLaunchKernelGGL((pad_transpose_kernel<T, BK>), dim3(nblk, (unsigned)(R / kTile)), dim3(256), 0, s,
+                         static_cast<const T*>(src), ld_src, col0, rows, offsets, w.poff, w.pblk_expert, (int)E,
+                         static_cast<T*>(dst), R);
+    }
+  };
+  pad_transpose(x_in, d, 0, a_rows, w.x_t, d);
+  pad_transpose(dy_perm, d, 0, nullptr, w.dy_t, d);
+  pad_transpose(w.h, F, 0, nullptr, w.h_t, F);
+  pad_transpose(w.dgu, 2 * F, 0, nullptr, w.dg_t, F);
+  pad_transpose(w.dgu, 2 * F, (int)F, nullptr, w.du_t, F);
 
   // weight gradients: one group per expert, k over its padded column range
   auto wgrad = [&](const void* A, int rows, const void* B, int N, float* C) {
