@@ -150,20 +150,6 @@ __global__ __launch_bounds__(256) void pad_transpose16_kernel(const uint16_t* __
       [&](int j, int c) { return blk + (int64_t)(cs + j * kTile + c) * kTile; });
 }
 
-// 16-bit elements: transpose_into_kernel in strips of up to 8 tiles along the
-// source columns (grid: strips x rows / 64 x batch).
-__global__ __launch_bounds__(256) void transpose_into16_kernel(const uint16_t* __restrict__ src, int rows, int cols,
-                                                               uint16_t* __restrict__ dst, int64_t ld_dst, int coff,
-                                                               int64_t dst_batch) {
-  const uint16_t* S = src + (int64_t)blockIdx.z * rows * cols;
-  uint16_t* D = dst + (int64_t)blockIdx.z * dst_batch;
-  const int r0 = blockIdx.y * kTile, cs = blockIdx.x * 8 * kTile;
-  const int ntile = min(8, cols / kTile - (int)blockIdx.x * 8);
-  transpose_strip16(
-      ntile, [&](int r) { return S + (int64_t)(r0 + r) * cols + cs; },
-      [&](int j, int c) { return D + (int64_t)(cs + j * kTile + c) * ld_dst + coff + r0; });
-}
-
 // dst[b][c * ld_dst + coff + r] = src[b][r * cols + c] for b < batch: transposes
 // of [rows, cols] matrices into column range [coff, coff + rows) of [cols, ld_dst].
 template <typename T>
@@ -218,17 +204,10 @@ hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const 
 
   // padded expert column ranges; transposed weights
   hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(1024), 0, s, offsets, (int)E, w.poff);
+  // (whole, regular matrices: one tile per block keeps the most tiles in flight)
   auto transpose_into = [&](const T* src, int rows, int cols, T* dst, int64_t ld_dst, int coff, int64_t batch) {
-    if constexpr (sizeof(T) == 2) {
-      const unsigned strips = (unsigned)((cols / kTile + 7) / 8);
-      hipLaunchKernelGGL(transpose_into16_kernel, dim3(strips, (unsigned)(rows / kTile), (unsigned)E), dim3(256), 0,
-                         s, reinterpret_cast<const uint16_t*>(src), rows, cols, reinterpret_cast<uint16_t*>(dst),
-                         ld_dst, coff, batch);
-    } else {
-      hipLaunchKernelGGL((transpose_into_kernel<T>), dim3((unsigned)(cols / kTile), (unsigned)(rows / kTile),
-                                                          (unsigned)E),
-                         dim3(256), 0, s, src, rows, cols, dst, ld_dst, coff, batch);
-    }
+    hipLaunchKernelGGL((transpose_into_kernel<T>), dim3((unsigned)(cols / kTile), (unsigned)(rows / kTile), (unsigned)E),
+                       dim3(256), 0, s, src, rows, cols, dst, ld_dst, coff, batch);
   };
   transpose_into(Wd, (int)d, (int)F, static_cast<T*>(w.wd_t), d, 0, F * d);
   transpose_into(Wg, (int)F, (int)d, static_cast<T*>(w.wgu_t), 2 * F, 0, d * 2 * F);
@@ -237,7 +216,7 @@ hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const 
   // dH = dY W_d (float32)
   GemmArgs a1 = args_grouped(dy_perm, nullptr, w.wd_t, nullptr, F * d, offsets, (int)E, n_max, (int)F, (int)d,
                              w.dh);
-  gemm<T, BK, EPI_F32_BIAS>(a1, num_cu, s);
+  gemm<T, BK, EPI_F32_BIAS>(a1, num_cu, s);   // (no bias; this instantiation runs faster here)
   // recompute G, U; dG | dU and H
   GemmArgs a2 = args_grouped(x_in, a_rows, w_gate, w_up, F * d, offsets, (int)E, n_max, (int)F, (int)d, w.dgu);
   a2.D = w.dh;
@@ -280,7 +259,7 @@ hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const 
     a.ksa = (int64_t)rows * BK;
     a.ksb = (int64_t)N * BK;
     a.kseg = w.poff;
-    gemm<T, BK, EPI_F32_BIAS, kFeatGroups | kFeatStrides>(a, num_cu, s);
+    gemm<T, BK, EPI_F32, kFeatGroups | kFeatStrides>(a, num_cu, s);
   };
   wgrad(w.dy_t, (int)d, w.h_t, (int)F, dw_down);
   wgrad(w.dg_t, (int)F, w.x_t, (int)d, dw_gate);

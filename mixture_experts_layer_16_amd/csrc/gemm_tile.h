@@ -27,7 +27,10 @@ namespace moe {
 
 enum GemmFeature { kFeatGroups = 1, kFeatStrides = 2 };
 
-enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2, EPI_AXPBY = 3, EPI_SWIGLU_BWD = 4 };
+enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2, EPI_AXPBY = 3, EPI_SWIGLU_BWD = 4, EPI_F32 = 5 };
+// float32 output: the accumulators plus an optional per-column bias (EPI_F32_BIAS),
+// or as they are (EPI_F32, which the compiler gives fewer registers)
+constexpr bool f32_epilogue(int epi) { return epi == EPI_F32_BIAS || epi == EPI_F32; }
 // Epilogues whose B tile holds gate rows and the matching up rows.
 constexpr bool paired_epilogue(int epi) { return epi == EPI_SWIGLU || epi == EPI_SWIGLU_BWD; }
 
@@ -483,8 +486,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
 
     const int h4 = 4 * (lane >> 5);
     // Staged through LDS, for an output element type OT (T, or float for
-    // EPI_F32_BIAS).
-    auto staged = [&](auto ot_tag) {
+    // EPI_F32 / EPI_F32_BIAS): val(mi, ni, q, i) is the value of element 4 q + i of output
+    // block (mi, ni), ni < NO; dstp the output matrix, row stride ld elements.
+    auto staged = [&](auto ot_tag, auto val, void* dstp, int64_t ld) {
       typedef typename decltype(ot_tag)::type OT;
       // Staged through LDS (wbuf: this wave's 32 rows x 144 bytes, which nothing
       // else touches until the next barrier).  Per round
@@ -506,8 +510,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
       const int r0 = wm * Cfg::WTM + (lane >> 3);
       const int rrem = erows - r0;
       const int c0l = en0 + wn * CW + (lane & 7) * (16 / ES);
-      OT* cbase = static_cast<OT*>(p.C) + (em0 + r0) * (int64_t)p.N + c0l;
-      const int64_t rstep = 8 * (int64_t)p.N;
+      OT* cbase = static_cast<OT*>(dstp) + (em0 + r0) * ld + c0l;
+      const int64_t rstep = 8 * ld;
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         if (mi >= mi_live) break;
@@ -521,18 +525,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
               if (c0 < 0 || c0 >= RC) continue;
               float v[4];
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                if constexpr (EPI == EPI_SWIGLU) {
-                  const float gv = acc[mi][ni][4 * q + i];
-                  const float uv = acc[mi][ni + NI / 2][4 * q + i];
-                  v[i] = gv / (1.0f + __expf(-gv)) * uv;
-                } else if constexpr (EPI == EPI_F32_BIAS) {
-                  const int col = en0 + wn * CW + ni * 32 + 8 * q + h4;
-                  v[i] = acc[mi][ni][4 * q + i] + ((p.bias && col + i < p.N) ? p.bias[col + i] : 0.f);
-                } else {
-                  v[i] = acc[mi][ni][4 * q + i];
-                }
-              }
+              for (int i = 0; i < 4; ++i) v[i] = val(mi, ni, q, i);
               store4(reinterpret_cast<OT*>(wlane + c0 * ES), v);
             }
           wait_lgkmcnt0();
@@ -540,7 +533,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
           for (int it = 0; it < 4; ++it) {
             const u32x4 val = *reinterpret_cast<const u32x4*>(rlane + it * 8 * RS);
             const int cc = c0l + rd * RC;
-            if constexpr (EPI == EPI_F32_BIAS) {
+            if constexpr (f32_epilogue(EPI)) {
               // N need not be a multiple of 4 here (a router's expert count)
               if (mi * 32 + it * 8 < rrem) {
                 OT* dst = cbase + (4 * mi + it) * rstep + rd * RC;
@@ -560,12 +553,28 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
         }
       }
     };
+    // (EPI_SWIGLU_BWD's three outputs stay on the direct path: staging them costs
+    // the K loop registers)
     constexpr bool kStaged = EPI != EPI_AXPBY && EPI != EPI_SWIGLU_BWD && NT == 512 && Cfg::WTM == 64 &&
                              8 * kEpiWaveBytes <= Cfg::kStageBytes;
     if constexpr (kStaged) {
-      staged(TypeTag<typename std::conditional<EPI == EPI_F32_BIAS, float, T>::type>{});
-    } else if constexpr (EPI == EPI_F32_BIAS) {
-      static_assert(EPI != EPI_F32_BIAS, "float32 outputs take the staged epilogue");
+      typedef typename std::conditional<f32_epilogue(EPI), float, T>::type OT;
+      staged(
+          TypeTag<OT>{},
+          [&](int mi, int ni, int q, int i) {
+            if constexpr (EPI == EPI_SWIGLU) {
+              const float gv = acc[mi][ni][4 * q + i];
+              return gv / (1.0f + __expf(-gv)) * acc[mi][ni + NI / 2][4 * q + i];
+            } else if constexpr (EPI == EPI_F32_BIAS) {
+              const int col = en0 + wn * Cfg::WTN + ni * 32 + 8 * q + h4 + i;
+              return acc[mi][ni][4 * q + i] + ((p.bias && col < p.N) ? p.bias[col] : 0.f);
+            } else {
+              return acc[mi][ni][4 * q + i];
+            }
+          },
+          p.C, (int64_t)p.N);
+    } else if constexpr (f32_epilogue(EPI)) {
+      static_assert(!f32_epilogue(EPI), "float32 outputs take the staged epilogue");
     } else {
       constexpr int NO = paired_epilogue(EPI) ? NI / 2 : NI;
       constexpr int CW = paired_epilogue(EPI) ? Cfg::WTN / 2 : Cfg::WTN;

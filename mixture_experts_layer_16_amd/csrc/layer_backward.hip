@@ -347,7 +347,7 @@ hipError_t route_backward_t(int64_t T_, int64_t d, int64_t E, int64_t k, const T
   a.ksa = E * BK;
   a.ksb = d * BK;
   a.kseg = ws.kseg;
-  hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, 4, 2, 2, EPI_F32_BIAS, 1, kFeatGroups | kFeatStrides>),
+  hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, 4, 2, 2, EPI_F32, 1, kFeatGroups | kFeatStrides>),
                      dim3(num_cu), dim3(512), 0, s, a);
   if (ws.splits > 1) {
     const int64_t n = E * d;

@@ -26,7 +26,6 @@
 #include "common.h"
 #include "gemm_tile.h"
 #include "kernels.h"
-#include "transpose.h"
 
 namespace moe {
 
@@ -82,18 +81,20 @@ __global__ __launch_bounds__(256) void ns_init_kernel(const bf16* __restrict__ g
   }
 }
 
-// dst[m] = src[m]^T for [rows, cols] bf16 matrices; strips of up to 8 tiles of
-// 64 x 64 (grid: strips along cols x rows / 64 x matrices).
+// dst[m] = src[m]^T for [rows, cols] bf16 matrices; one 64 x 64 tile per block
+// (for these whole, regular matrices one tile per block keeps more tiles in
+// flight than the strip transposes, which pay off where rows are looked up).
 __global__ __launch_bounds__(256) void ns_transpose_kernel(const bf16* __restrict__ src, int rows, int cols,
                                                            bf16* __restrict__ dst) {
+  __shared__ bf16 tile[kTile][kTile + 2];
   const int64_t per = (int64_t)rows * cols;
-  const uint16_t* S = reinterpret_cast<const uint16_t*>(src) + blockIdx.z * per;
-  uint16_t* D = reinterpret_cast<uint16_t*>(dst) + blockIdx.z * per;
-  const int r0 = blockIdx.y * kTile, cs = blockIdx.x * 8 * kTile;
-  const int ntile = min(8, cols / kTile - (int)blockIdx.x * 8);
-  transpose_strip16(
-      ntile, [&](int r) { return S + (int64_t)(r0 + r) * cols + cs; },
-      [&](int j, int c) { return D + (int64_t)(cs + j * kTile + c) * rows + r0; });
+  const bf16* S = src + blockIdx.z * per;
+  bf16* D = dst + blockIdx.z * per;
+  const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < kTile; i += 4) tile[i][tx] = S[(int64_t)(r0 + i) * cols + c0 + tx];
+  __syncthreads();
+  for (int i = ty; i < kTile; i += 4) D[(int64_t)(c0 + i) * rows + r0 + tx] = tile[tx][i];
 }
 
 GemmArgs batch_gemm(const bf16* A, const bf16* B, int64_t b_stride, int n, int64_t rows, int N, int K, bf16* C) {
@@ -162,7 +163,7 @@ hipError_t launch_newton_schulz(int64_t n, int64_t R, int64_t C, int64_t steps, 
                        dim3(WM * WN * 64), 0, stream, p3);
     if (last && tall) break;
     // Xw = Xt'^T (the result itself on the last step of a wide matrix)
-    hipLaunchKernelGGL(ns_transpose_kernel, dim3((unsigned)((Rw / kTile + 7) / 8), (unsigned)(Cw / kTile), (unsigned)n),
+    hipLaunchKernelGGL(ns_transpose_kernel, dim3((unsigned)(Rw / kTile), (unsigned)(Cw / kTile), (unsigned)n),
                        dim3(256), 0, stream, out, (int)Cw, (int)Rw, last ? X : Xw);
     cur ^= 1;
   }
