@@ -423,7 +423,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
 
   // ---- MFMA operand fragments: one buffer per sub-step of a k-tile, read PD
   //      sub-steps ahead of the MFMAs that use them -------------------------------
-  typename Op::Frag fa[KSUB][MI], fb[KSUB][NI];
+  // Sub-step s reads buffer s % NBUF and fills buffer (s + PD) % NBUF: PD + 1
+  // buffers are all that is ever live (KSUB is a multiple of NBUF), and the smaller
+  // register footprint keeps the K loop free of spills.
+  constexpr int NBUF = PD + 1;
+  static_assert(KSUB % NBUF == 0, "the fragment ring wraps at k-tile boundaries");
+  typename Op::Frag fa[NBUF][MI], fb[NBUF][NI];
   // full: every row block of this wave is live (no per-block checks)
   auto read_frags = [&](bool full, int buf, int stage, int sub) {
     const char* sA = smem + stage * Cfg::kStageBytes;
@@ -434,17 +439,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
       if (!full && mi >= mi_live) continue;
       const int r = wm * Cfg::WTM + mi * 32 + (lane & 31);
       if constexpr (Op::kReads == 1)
-        Op::load(fa[buf][mi], sA + r * RB + Cfg::swz(r, lc0) * 16);
+        Op::load(fa[buf % NBUF][mi], sA + r * RB + Cfg::swz(r, lc0) * 16);
       else
-        Op::load(fa[buf][mi], sA + r * RB + Cfg::swz(r, lc0) * 16, sA + r * RB + Cfg::swz(r, lc0 + 1) * 16);
+        Op::load(fa[buf % NBUF][mi], sA + r * RB + Cfg::swz(r, lc0) * 16, sA + r * RB + Cfg::swz(r, lc0 + 1) * 16);
     }
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
       const int r = Cfg::b_row(wn, ni) + (lane & 31);
       if constexpr (Op::kReads == 1)
-        Op::load(fb[buf][ni], sB + r * RB + Cfg::swz(r, lc0) * 16);
+        Op::load(fb[buf % NBUF][ni], sB + r * RB + Cfg::swz(r, lc0) * 16);
       else
-        Op::load(fb[buf][ni], sB + r * RB + Cfg::swz(r, lc0) * 16, sB + r * RB + Cfg::swz(r, lc0 + 1) * 16);
+        Op::load(fb[buf % NBUF][ni], sB + r * RB + Cfg::swz(r, lc0) * 16, sB + r * RB + Cfg::swz(r, lc0 + 1) * 16);
     }
   };
   f32x16 acc[MI][NI];
@@ -455,7 +460,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     for (int mi = 0; mi < MI; ++mi)
       if (full || mi < mi_live) {
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) Op::mma(fb[buf][ni], fa[buf][mi], acc[mi][ni]);
+        for (int ni = 0; ni < NI; ++ni) Op::mma(fb[buf % NBUF][ni], fa[buf % NBUF][mi], acc[mi][ni]);
       }
   };
   // the same MFMAs with copies J0 .. J1-1 of k-tile kt into `stage` (if copy)
@@ -467,7 +472,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
-        if (full || mi < mi_live) Op::mma(fb[buf][ni], fa[buf][mi], acc[mi][ni]);
+        if (full || mi < mi_live) Op::mma(fb[buf % NBUF][ni], fa[buf % NBUF][mi], acc[mi][ni]);
         const int q = mi * NI + ni;
         // copies go after MFMAs q with q * NJ / NM stepping up
 #pragma unroll
