@@ -216,7 +216,7 @@ hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const 
   // dH = dY W_d (float32)
   GemmArgs a1 = args_grouped(dy_perm, nullptr, w.wd_t, nullptr, F * d, offsets, (int)E, n_max, (int)F, (int)d,
                              w.dh);
-  gemm<T, BK, EPI_F32_BIAS>(a1, num_cu, s);   // (no bias; this instantiation runs faster here)
+  gemm<T, BK, EPI_F32>(a1, num_cu, s);
   // recompute G, U; dG | dU and H
   GemmArgs a2 = args_grouped(x_in, a_rows, w_gate, w_up, F * d, offsets, (int)E, n_max, (int)F, (int)d, w.dgu);
   a2.D = w.dh;

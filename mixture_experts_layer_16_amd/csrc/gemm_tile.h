@@ -29,7 +29,7 @@ enum GemmFeature { kFeatGroups = 1, kFeatStrides = 2 };
 
 enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2, EPI_AXPBY = 3, EPI_SWIGLU_BWD = 4, EPI_F32 = 5 };
 // float32 output: the accumulators plus an optional per-column bias (EPI_F32_BIAS),
-// or as they are (EPI_F32, which the compiler gives fewer registers)
+// or as they are (EPI_F32)
 constexpr bool f32_epilogue(int epi) { return epi == EPI_F32_BIAS || epi == EPI_F32; }
 // Epilogues whose B tile holds gate rows and the matching up rows.
 constexpr bool paired_epilogue(int epi) { return epi == EPI_SWIGLU || epi == EPI_SWIGLU_BWD; }
