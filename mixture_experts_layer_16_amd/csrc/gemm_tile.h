@@ -49,9 +49,10 @@ constexpr int kXcds = 8;   // accelerator complex dies of an MI355X, one L2 each
 // A recycled stage's copies are threaded between the MFMAs of the kDmaSpread
 // sub-steps that follow the barrier (0: all issued at the barrier).  Issued as one
 // burst, the copies of eight waves queue up in the vector-memory path and hold up
-// the MFMAs behind them in every wave.
+// the MFMAs behind them in every wave; two sub-steps measured 1-2% faster than one
+// (and 4% faster than none) on the page-shape grouped FFN and its backward.
 #ifndef MOE_DMA_SPREAD
-#define MOE_DMA_SPREAD 1
+#define MOE_DMA_SPREAD 2
 #endif
 constexpr int kDmaSpread = MOE_DMA_SPREAD;
 
