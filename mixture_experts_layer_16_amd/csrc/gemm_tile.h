@@ -187,6 +187,32 @@ __device__ __forceinline__ void store4(float* p, const float* v) {
   *reinterpret_cast<f32x4*>(p) = q;
 }
 
+// Direct epilogue stores of 16-bit outputs, 16 bytes per lane.  For two consecutive
+// 8-column groups of one row, lane l holds columns 0-3 of each (a: the first group,
+// b: the second) and lane l + 32 columns 4-7; one exchange across the halves gives
+// lane l the first group's 8 values and lane l + 32 the second group's.  Returns
+// this lane's 8 values (as bf16 bit patterns) to store at group (lane < 32 ? 0 : 1).
+__device__ __forceinline__ u32x4 pair_groups16(const float* a, const float* b, int lane) {
+  auto pack = [](float x, float y) {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+    bf16x2 v;
+    v[0] = static_cast<bf16>(x);
+    v[1] = static_cast<bf16>(y);
+    return __builtin_bit_cast(uint32_t, v);
+  };
+  const uint32_t a0 = pack(a[0], a[1]), a1 = pack(a[2], a[3]);
+  const uint32_t b0 = pack(b[0], b[1]), b1 = pack(b[2], b[3]);
+  const bool lo = lane < 32;
+  const uint32_t r0 = (uint32_t)__shfl_xor((int)(lo ? b0 : a0), 32, 64);
+  const uint32_t r1 = (uint32_t)__shfl_xor((int)(lo ? b1 : a1), 32, 64);
+  u32x4 out;
+  out[0] = lo ? a0 : r0;
+  out[1] = lo ? a1 : r1;
+  out[2] = lo ? r0 : b0;
+  out[3] = lo ? r1 : b1;
+  return out;
+}
+
 template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI>
 struct GemmTile {
   static constexpr int kThreads = WM * WN * 64;
@@ -588,52 +614,78 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         const int r = wm * Cfg::WTM + mi * 32 + (lane & 31);
-        if (r >= erows) continue;
+        if (r >= erows) continue;               // (lanes l and l + 32 share the row)
         T* crow = static_cast<T*>(p.C) + (em0 + r) * ldc;
 #pragma unroll
         for (int ni = 0; ni < NO; ++ni)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int col = en0 + wn * CW + ni * 32 + 8 * q + h4;
-            if constexpr (EPI == EPI_SWIGLU_BWD) {
-              // recomputed G and U with the incoming dH:  S = silu(G), H = S U,
-              // dU = dH S, dG = dH U silu'(G); dG and dU go to the row's two halves
-              if (col < p.N) {
-                const f32x4 dh =
-                    *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.D) + (em0 + r) * (int64_t)p.N + col);
-                float dg[4], du[4], hh[4];
+          for (int q = 0; q < 4; q += 2) {
+            // two 8-column groups q, q + 1; N is a multiple of 8 here, so both lanes of
+            // a pair agree on every column test
+            float v[2][3][4];                     // [group][output][element]
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+              const int col = en0 + wn * CW + ni * 32 + 8 * (q + qq) + h4;
+              if constexpr (EPI == EPI_SWIGLU_BWD) {
+                // recomputed G and U with the incoming dH:  S = silu(G), H = S U,
+                // dU = dH S, dG = dH U silu'(G); dG and dU go to the row's two halves
+                f32x4 dh = {0.f, 0.f, 0.f, 0.f};
+                if (col < p.N)
+                  dh = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.D) + (em0 + r) * (int64_t)p.N +
+                                                       col);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                  const float g = acc[mi][ni][4 * q + i];
-                  const float u = acc[mi][ni + NI / 2][4 * q + i];
+                  const float g = acc[mi][ni][4 * (q + qq) + i];
+                  const float u = acc[mi][ni + NI / 2][4 * (q + qq) + i];
                   const float sg = 1.0f / (1.0f + __expf(-g));
                   const float sv = g * sg;
-                  du[i] = dh[i] * sv;
-                  dg[i] = dh[i] * u * (sg * (1.0f + g * (1.0f - sg)));
-                  hh[i] = sv * u;
+                  v[qq][0][i] = dh[i] * u * (sg * (1.0f + g * (1.0f - sg)));
+                  v[qq][1][i] = dh[i] * sv;
+                  v[qq][2][i] = sv * u;
                 }
-                store4(crow + col, dg);
-                store4(crow + p.N + col, du);
-                store4(static_cast<T*>(p.C2) + (em0 + r) * (int64_t)p.N + col, hh);
-              }
-            } else if (col < p.N) {
-              float v[4];
-              float dv[4] = {0.f, 0.f, 0.f, 0.f};
-              if constexpr (EPI == EPI_AXPBY)
-                load4(static_cast<const T*>(p.D) + (em0 + r) * (int64_t)p.N + col, dv);
+              } else {
+                float dv[4] = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (EPI == EPI_AXPBY)
+                  if (col < p.N) load4(static_cast<const T*>(p.D) + (em0 + r) * (int64_t)p.N + col, dv);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                if constexpr (EPI == EPI_SWIGLU) {
-                  const float gv = acc[mi][ni][4 * q + i];
-                  const float uv = acc[mi][ni + NI / 2][4 * q + i];
-                  v[i] = gv / (1.0f + __expf(-gv)) * uv;
-                } else if constexpr (EPI == EPI_AXPBY) {
-                  v[i] = p.alpha * acc[mi][ni][4 * q + i] + p.beta * dv[i];
-                } else {
-                  v[i] = acc[mi][ni][4 * q + i];
+                for (int i = 0; i < 4; ++i) {
+                  if constexpr (EPI == EPI_SWIGLU) {
+                    const float gv = acc[mi][ni][4 * (q + qq) + i];
+                    const float uv = acc[mi][ni + NI / 2][4 * (q + qq) + i];
+                    v[qq][0][i] = gv / (1.0f + __expf(-gv)) * uv;
+                  } else if constexpr (EPI == EPI_AXPBY) {
+                    v[qq][0][i] = p.alpha * acc[mi][ni][4 * (q + qq) + i] + p.beta * dv[i];
+                  } else {
+                    v[qq][0][i] = acc[mi][ni][4 * (q + qq) + i];
+                  }
                 }
               }
-              store4(crow + col, v);
+            }
+            constexpr int NOUT_ = EPI == EPI_SWIGLU_BWD ? 3 : 1;
+            if constexpr (sizeof(T) == 2) {
+              const int colp = en0 + wn * CW + ni * 32 + 8 * (q + (lane >> 5));   // this lane's 8 columns
+#pragma unroll
+              for (int o = 0; o < NOUT_; ++o) {
+                const u32x4 w = pair_groups16(v[0][o], v[1][o], lane);
+                if (colp < p.N) {
+                  T* dst = o == 0 ? crow + colp
+                                  : (o == 1 ? crow + p.N + colp : static_cast<T*>(p.C2) + (em0 + r) * (int64_t)p.N + colp);
+                  *reinterpret_cast<u32x4*>(dst) = w;
+                }
+              }
+            } else {
+#pragma unroll
+              for (int qq = 0; qq < 2; ++qq) {
+                const int col = en0 + wn * CW + ni * 32 + 8 * (q + qq) + h4;
+                if (col < p.N) {
+#pragma unroll
+                  for (int o = 0; o < NOUT_; ++o) {
+                    T* dst = o == 0 ? crow + col
+                                    : (o == 1 ? crow + p.N + col : static_cast<T*>(p.C2) + (em0 + r) * (int64_t)p.N + col);
+                    store4(dst, v[qq][o]);
+                  }
+                }
+              }
             }
           }
       }
