@@ -623,6 +623,30 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
             // two 8-column groups q, q + 1; N is a multiple of 8 here, so both lanes of
             // a pair agree on every column test
             float v[2][3][4];                     // [group][output][element]
+            // EPI_AXPBY with 16-bit D: this lane loads the 8 values of D at its
+            // store columns (16 bytes) and the pair exchanges halves back into
+            // the MFMA layout: dd[qq] = columns 8 (q + qq) + h4 .. + 3
+            float dd[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            if constexpr (EPI == EPI_AXPBY && sizeof(T) == 2) {
+              const int colp = en0 + wn * CW + ni * 32 + 8 * (q + (lane >> 5));
+              u32x4 ld = {0u, 0u, 0u, 0u};
+              if (colp < p.N)
+                ld = *reinterpret_cast<const u32x4*>(static_cast<const T*>(p.D) + (em0 + r) * (int64_t)p.N + colp);
+              const bool lo = lane < 32;
+              // lane l keeps columns 0-3 of group q and needs 0-3 of group q + 1 (the
+              // partner's first half); lane l + 32 keeps 4-7 of group q + 1 and needs
+              // 4-7 of group q (the partner's second half)
+              const uint32_t s0 = lo ? ld[2] : ld[0], s1 = lo ? ld[3] : ld[1];
+              const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32, 64), r1 = (uint32_t)__shfl_xor((int)s1, 32, 64);
+              const uint32_t own0 = lo ? ld[0] : ld[2], own1 = lo ? ld[1] : ld[3];
+              auto lo16 = [](uint32_t w) { return __uint_as_float(w << 16); };
+              auto hi16 = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
+              // lo lane: group q = own, group q + 1 = received; hi lane: group q = received
+              const uint32_t g0a = lo ? own0 : r0, g0b = lo ? own1 : r1;
+              const uint32_t g1a = lo ? r0 : own0, g1b = lo ? r1 : own1;
+              dd[0][0] = lo16(g0a); dd[0][1] = hi16(g0a); dd[0][2] = lo16(g0b); dd[0][3] = hi16(g0b);
+              dd[1][0] = lo16(g1a); dd[1][1] = hi16(g1a); dd[1][2] = lo16(g1b); dd[1][3] = hi16(g1b);
+            }
 #pragma unroll
             for (int qq = 0; qq < 2; ++qq) {
               const int col = en0 + wn * CW + ni * 32 + 8 * (q + qq) + h4;
@@ -644,8 +668,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
                   v[qq][2][i] = sv * u;
                 }
               } else {
-                float dv[4] = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (EPI == EPI_AXPBY)
+                float dv[4] = {dd[qq][0], dd[qq][1], dd[qq][2], dd[qq][3]};
+                if constexpr (EPI == EPI_AXPBY && sizeof(T) != 2)
                   if (col < p.N) load4(static_cast<const T*>(p.D) + (em0 + r) * (int64_t)p.N + col, dv);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
