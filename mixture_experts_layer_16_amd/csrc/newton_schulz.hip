@@ -33,17 +33,22 @@ namespace {
 
 constexpr int kTile = 64;
 
-// partial[m * kNormBlocks + b] = sum of squares of chunk b of matrix m
+// partial[m * kNormBlocks + b] = sum of squares of chunk b of matrix m (chunks of
+// per / kNormBlocks elements, a multiple of 8: R and C are multiples of 64), read as
+// 16-byte vectors; each thread's running sum, then a fixed-order block reduction.
 __global__ __launch_bounds__(256) void ns_sumsq_kernel(const bf16* __restrict__ g, int64_t per, float* __restrict__ partial) {
   __shared__ float wsum[4];
   const int m = blockIdx.y, b = blockIdx.x;
-  const int64_t chunk = (per + kNormBlocks - 1) / kNormBlocks;
-  const int64_t lo = min<int64_t>(per, (int64_t)b * chunk), hi = min<int64_t>(per, lo + chunk);
-  const bf16* p = g + (int64_t)m * per;
+  const int64_t chunk = per / kNormBlocks;
+  const bf16* p = g + (int64_t)m * per + (int64_t)b * chunk;
   float s = 0.f;
-  for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
-    const float v = static_cast<float>(p[i]);
-    s = fmaf(v, v, s);
+  for (int64_t i = (int64_t)threadIdx.x * 8; i < chunk; i += 256 * 8) {
+    const bf16x8 q = *reinterpret_cast<const bf16x8*>(p + i);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = static_cast<float>(q[j]);
+      s = fmaf(v, v, s);
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
@@ -53,32 +58,53 @@ __global__ __launch_bounds__(256) void ns_sumsq_kernel(const bf16* __restrict__ 
 }
 
 // scale = 1 / (sqrt(sum of the partials in order) + eps); out_same = scale * G (G's
-// orientation), out_t = its transpose.  One 64 x 64 tile of one matrix per block.
+// orientation), out_t = its transpose, both rounded once to bf16.  One 64 x 64 tile
+// of one matrix per block: each thread reads 16 consecutive elements of one row
+// (two 16-byte loads), writes them scaled in place order, and parks them in LDS
+// column-wise; then reads 16 consecutive elements of one transposed row.
 __global__ __launch_bounds__(256) void ns_init_kernel(const bf16* __restrict__ g, int R, int C,
                                                       const float* __restrict__ partial, float eps,
                                                       bf16* __restrict__ out_same, bf16* __restrict__ out_t) {
-  __shared__ float tile[kTile][kTile + 1];
+  __shared__ uint16_t tile[kTile][kTile + 2];
   const int m = blockIdx.z;
   float ss = 0.f;
   for (int i = 0; i < kNormBlocks; ++i) ss += partial[(int64_t)m * kNormBlocks + i];
   const float scale = 1.0f / (sqrtf(ss) + eps);
   const int64_t per = (int64_t)R * C;
-  const bf16* G = g + m * per;
-  bf16* S = out_same + m * per;
-  bf16* Tt = out_t + m * per;
   const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < kTile; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    const float v = static_cast<float>(G[(int64_t)r * C + c]) * scale;
-    tile[i][tx] = v;
-    S[(int64_t)r * C + c] = static_cast<bf16>(v);
+  const int t = threadIdx.x, r = t >> 2, q = (t & 3) * 16;
+  const int64_t off = m * per + (int64_t)(r0 + r) * C + c0 + q;
+  bf16x8 v[2];
+  v[0] = *reinterpret_cast<const bf16x8*>(g + off);
+  v[1] = *reinterpret_cast<const bf16x8*>(g + off + 8);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[h][j] = static_cast<bf16>(static_cast<float>(v[h][j]) * scale);
+  // park the 16 rounded values column-wise (halves taken from the packed words)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const u32x4 w = __builtin_bit_cast(u32x4, v[h]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[q + 8 * h + 2 * e][r] = (uint16_t)(w[e] & 0xffffu);
+      tile[q + 8 * h + 2 * e + 1][r] = (uint16_t)(w[e] >> 16);
+    }
   }
+  *reinterpret_cast<bf16x8*>(out_same + off) = v[0];
+  *reinterpret_cast<bf16x8*>(out_same + off + 8) = v[1];
   __syncthreads();
-  for (int i = ty; i < kTile; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    Tt[(int64_t)c * R + r] = static_cast<bf16>(tile[tx][i]);
+  const int c = t >> 2, p = (t & 3) * 16;
+  const uint32_t* row = reinterpret_cast<const uint32_t*>(&tile[c][0]) + p / 2;
+  u32x4 o0, o1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o0[e] = row[e];
+    o1[e] = row[4 + e];
   }
+  uint16_t* d = reinterpret_cast<uint16_t*>(out_t) + m * per + (int64_t)(c0 + c) * R + r0 + p;
+  *reinterpret_cast<u32x4*>(d) = o0;
+  *reinterpret_cast<u32x4*>(d + 8) = o1;
 }
 
 // dst[m] = src[m]^T for [rows, cols] bf16 matrices; one 64 x 64 tile per block
