@@ -563,22 +563,22 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
           wait_lgkmcnt0();
 #pragma unroll
           for (int it = 0; it < 4; ++it) {
-            const u32x4 val = *reinterpret_cast<const u32x4*>(rlane + it * 8 * RS);
+            const u32x4 piece = *reinterpret_cast<const u32x4*>(rlane + it * 8 * RS);
             const int cc = c0l + rd * RC;
             if constexpr (f32_epilogue(EPI)) {
               // N need not be a multiple of 4 here (a router's expert count)
               if (mi * 32 + it * 8 < rrem) {
                 OT* dst = cbase + (4 * mi + it) * rstep + rd * RC;
                 if (cc + 16 / ES <= p.N) {
-                  *reinterpret_cast<u32x4*>(dst) = val;
+                  *reinterpret_cast<u32x4*>(dst) = piece;
                 } else if (cc < p.N) {
-                  const OT* ev = reinterpret_cast<const OT*>(&val);
+                  const OT* ev = reinterpret_cast<const OT*>(&piece);
                   for (int i = 0; i < 16 / ES && cc + i < p.N; ++i) dst[i] = ev[i];
                 }
               }
             } else {
               if (mi * 32 + it * 8 < rrem && cc < p.N)
-                *reinterpret_cast<u32x4*>(cbase + (4 * mi + it) * rstep + rd * RC) = val;
+                *reinterpret_cast<u32x4*>(cbase + (4 * mi + it) * rstep + rd * RC) = piece;
             }
           }
           wait_lgkmcnt0();
