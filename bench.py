@@ -304,7 +304,7 @@ def bench_backward(args, torch, B, W):
                    "top_k": wl.k, "expert_hidden": wl.F, "slots": n},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "grouped expert-FFN backward (7 GEMM launches, weight and activation transposes)",
+                     "kernel": "grouped expert-FFN backward (7 GEMM launches, activation transposes; weights read in place)",
                      "flops_per_launch": flops, "ms_per_launch": round(ffn_ms, 4),
                      "note": "achieved counts 12 N d F; the G/U recompute (4 N d F) is extra work"},
         "stages_ms": {k_: round(v, 4) for k_, v in stages.items()},

@@ -175,9 +175,10 @@ moe_status moe_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
  *   dx_perm  [n_max,d] dtype   out: dX (first offsets[E] rows written)
  *   dw_gate, dw_up [E,F,d] f32, dw_down [E,d,F] f32   out; zero for an expert with
  *                        no rows
- *   ws: query with ws == NULL (holds transposed weights, dH in float32, dG|dU,
- *       H and transposed activations: about 3 E d F + 4 n_max F dtype elements,
- *       n_max F float32, and 2 (d + 3 F) (n_max + 63 E) dtype elements).
+ *   ws: query with ws == NULL (holds dH in float32, dG|dU, H and transposed
+ *       activations: 3 n_max F dtype elements, n_max F float32 and
+ *       (2 d + 3 F) (n_max + 63 E) dtype elements; float32 layers add transposed
+ *       weight copies, 3 E d F elements; bf16 weights are read in place).
  * bf16: bf16 products, float32 accumulation; dG, dU and H are rounded to bf16
  * before the products that use them.  float32: float32 throughout.
  * Errors as moe_grouped_ffn.

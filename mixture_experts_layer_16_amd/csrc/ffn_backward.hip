@@ -9,11 +9,12 @@
 //     dX = dG W_g + dU W_u
 //     dW_d = dY^T H,   dW_g = dG^T X,   dW_u = dU^T X
 //
-// Everything runs on the grouped NT GEMM (C = A B^T, both operands read along
-// the contraction):
-//   * dH = dY (W_d^T)^T and dX = [dG | dU] [W_g^T ; W_u^T]^T read transposed
-//     copies of the weights ([E, F, d] and [E, d, 2F], made here, bandwidth-
-//     bound), in float32 (dH) and the I/O type (dX);
+// Everything runs on the grouped GEMM (C = A B^T, both operands read along the
+// contraction, or C = A B with B stored along N):
+//   * dH = dY W_d and dX = [dG | dU] [W_g ; W_u] contract along the weights'
+//     first dimension: 16-bit weights are read in place (the GEMM's B-along-N
+//     form, transposing LDS reads), float32 ones through transposed copies
+//     ([E, F, d] and [E, d, 2F], made here); dH is float32, dX the I/O type;
 //   * the I/O type is bf16 (MFMA bf16 products, float32 accumulation) or float32
 //     (float32 MFMA products throughout);
 //   * G and U are recomputed by the gate/up GEMM, whose epilogue turns them and
@@ -209,24 +210,40 @@ hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const 
     hipLaunchKernelGGL((transpose_into_kernel<T>), dim3((unsigned)(cols / kTile), (unsigned)(rows / kTile), (unsigned)E),
                        dim3(256), 0, s, src, rows, cols, dst, ld_dst, coff, batch);
   };
-  transpose_into(Wd, (int)d, (int)F, static_cast<T*>(w.wd_t), d, 0, F * d);
-  transpose_into(Wg, (int)F, (int)d, static_cast<T*>(w.wgu_t), 2 * F, 0, d * 2 * F);
-  transpose_into(Wu, (int)F, (int)d, static_cast<T*>(w.wgu_t), 2 * F, (int)F, d * 2 * F);
+  // 16-bit weights are read where they lie (B stored along N, transposing LDS
+  // reads); float32 ones through transposed copies
+  constexpr bool kBkn = sizeof(T) == 2;
+  if constexpr (!kBkn) {
+    transpose_into(Wd, (int)d, (int)F, static_cast<T*>(w.wd_t), d, 0, F * d);
+    transpose_into(Wg, (int)F, (int)d, static_cast<T*>(w.wgu_t), 2 * F, 0, d * 2 * F);
+    transpose_into(Wu, (int)F, (int)d, static_cast<T*>(w.wgu_t), 2 * F, (int)F, d * 2 * F);
+  }
 
   // dH = dY W_d (float32)
-  GemmArgs a1 = args_grouped(dy_perm, nullptr, w.wd_t, nullptr, F * d, offsets, (int)E, n_max, (int)F, (int)d,
-                             w.dh);
-  gemm<T, BK, EPI_F32>(a1, num_cu, s);
+  if constexpr (kBkn) {
+    GemmArgs a1 = args_grouped(dy_perm, nullptr, Wd, nullptr, d * F, offsets, (int)E, n_max, (int)F, (int)d, w.dh);
+    gemm<T, BK, EPI_F32, kFeatBKN>(a1, num_cu, s);
+  } else {
+    GemmArgs a1 = args_grouped(dy_perm, nullptr, w.wd_t, nullptr, F * d, offsets, (int)E, n_max, (int)F, (int)d,
+                               w.dh);
+    gemm<T, BK, EPI_F32>(a1, num_cu, s);
+  }
   // recompute G, U; dG | dU and H
   GemmArgs a2 = args_grouped(x_in, a_rows, w_gate, w_up, F * d, offsets, (int)E, n_max, (int)F, (int)d, w.dgu);
   a2.D = w.dh;
   a2.C2 = w.h;
   a2.ldc = 2 * F;
   gemm<T, BK, EPI_SWIGLU_BWD>(a2, num_cu, s);
-  // dX = [dG | dU] [W_g^T ; W_u^T]^T
-  GemmArgs a3 = args_grouped(w.dgu, nullptr, w.wgu_t, nullptr, d * 2 * F, offsets, (int)E, n_max, (int)d,
-                             (int)(2 * F), dx_perm);
-  gemm<T, BK, EPI_STORE>(a3, num_cu, s);
+  // dX = [dG | dU] [W_g ; W_u]: k < F reads W_g's rows, k >= F W_u's
+  if constexpr (kBkn) {
+    GemmArgs a3 = args_grouped(w.dgu, nullptr, Wg, Wu, F * d, offsets, (int)E, n_max, (int)d, (int)(2 * F), dx_perm);
+    a3.k_split = (int32_t)F;
+    gemm<T, BK, EPI_STORE, kFeatBKN>(a3, num_cu, s);
+  } else {
+    GemmArgs a3 = args_grouped(w.dgu, nullptr, w.wgu_t, nullptr, d * 2 * F, offsets, (int)E, n_max, (int)d,
+                               (int)(2 * F), dx_perm);
+    gemm<T, BK, EPI_STORE>(a3, num_cu, s);
+  }
 
   // transposed, padded, k-blocked activations for the weight gradients
   const unsigned nblk = (unsigned)(np / kTile);

@@ -25,7 +25,7 @@
 
 namespace moe {
 
-enum GemmFeature { kFeatGroups = 1, kFeatStrides = 2 };
+enum GemmFeature { kFeatGroups = 1, kFeatStrides = 2, kFeatBKN = 4 };
 
 enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2, EPI_AXPBY = 3, EPI_SWIGLU_BWD = 4, EPI_F32 = 5 };
 // float32 output: the accumulators plus an optional per-column bias (EPI_F32_BIAS),
@@ -88,6 +88,8 @@ struct GemmArgs {
                           // (0: BK).  With lda = BK and ksa = rows * BK, A is stored
                           // k-blocked: slice j is a contiguous [rows, BK] block, so a
                           // tile's k-step reads one contiguous piece of memory
+  int32_t k_split;        // kFeatBKN: k-slices at k >= k_split come from B1 (its rows
+                          // k - k_split); 0: every k-slice comes from B0
 };
 
 // Per element type: how one wave multiplies a 32x32 block over 16 k values.
@@ -138,6 +140,20 @@ __device__ __forceinline__ void lds_dma16(const char* gbase, uint32_t voff, uint
       : "=&s"(saved)
       : "v"(voff), "s"(gbase), "s"(lds_addr)
       : "memory");
+}
+// gfx950 transposing LDS read (ds_read_b64_tr_b16), twice.  Within each 16-lane
+// group, lane i receives element i % 4 of the 8-byte pieces that lanes i / 4,
+// 4 + i / 4, 8 + i / 4 and 12 + i / 4 of the group point at: with lane 4 j + m
+// pointing at row j, columns 4 m .. 4 m + 3 of a row-major 16-bit tile, lane i
+// gets column i of rows 0 .. 3.  The second read starts `stride` bytes further;
+// its 4 values follow the first read's in the result.
+__device__ __forceinline__ bf16x8 read_tr16x2(const char* p, int stride) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS s16x4*)const_cast<char*>(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS s16x4*)const_cast<char*>(p + stride));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
 }
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -287,6 +303,10 @@ __device__ void build_tile_prefix(const int32_t* seg, int G, int64_t M, int64_t 
 // FEAT (compile-time, so that kernels without them compile as if absent):
 //   kFeatGroups:  equal groups without offsets (seg == nullptr, group_rows > 0);
 //   kFeatStrides: lda, ldb, ksa, ksb, kseg and a_shared;
+//   kFeatBKN:     16-bit B stored along N: group g's B is [K, N] (row stride N), so
+//                 C = A B instead of A B^T (k_split: see GemmArgs).  A B k-slice goes
+//                 to LDS as it lies in memory (BK rows of BN columns) and the MFMA
+//                 operand fragments come out of gfx950's transposing LDS read;
 // otherwise those fields are ignored: operands are [rows, K] with one K for every
 // group, and the groups come from seg (or are one group of M rows).
 template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int EPI, int PD = 1, int FEAT = 0>
@@ -302,6 +322,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   constexpr int KSUB = Cfg::kSub;
   static_assert(PD >= 1 && PD < KSUB, "prefetch distance must be 1 .. sub-steps - 1");
   constexpr bool GRP = (FEAT & kFeatGroups) != 0, STR = (FEAT & kFeatStrides) != 0;
+  constexpr bool BKN = (FEAT & kFeatBKN) != 0;
+  static_assert(!BKN || (sizeof(T) == 2 && !paired_epilogue(EPI) && !STR && Cfg::kSub * 16 == BK && BN % 128 == 0),
+                "B along N: 16-bit elements, one B per output column block, BN a multiple of 128");
+  // B along N: each LDS row of the B region is one k value, BN columns (RBN bytes,
+  // 16-byte chunks).  Chunk c of row k sits at chunk c ^ (4 (k % 4)): the
+  // transposing read takes 4 consecutive k rows at once, and the XOR moves them to
+  // four distinct 64-byte bank groups.
+  constexpr int RBN = BN * 2;
 
   constexpr int kEpiRowBytes = 144;                 // staging row stride of the epilogue (bytes)
   constexpr int kEpiWaveBytes = 32 * kEpiRowBytes;  // one wave's staging buffer: 32 rows
@@ -395,15 +423,32 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     const int64_t k0 = STR ? t.k0 : 0;
     const int64_t ka0 = (STR && p.ksa) ? k0 / BK * p.ksa : k0, kb0 = (STR && p.ksb) ? k0 / BK * p.ksb : k0;
     Ab = reinterpret_cast<const char*>(Abase + ka0 + (p.a_rows ? 0 : ((STR && p.a_shared) ? t.mrel : t.m0) * lda));
-    Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)t.g * p.b_stride + (int64_t)t.n0 * ldb +
-                                        kb0);
-    if (paired_epilogue(EPI))
-      Bub = reinterpret_cast<const char*>(static_cast<const T*>(p.B1) + (int64_t)t.g * p.b_stride +
+    if constexpr (BKN) {
+      // [K, N]: the tile's columns start n0 elements into every k row
+      Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)t.g * p.b_stride + t.n0);
+      if (p.k_split > 0)
+        Bub = reinterpret_cast<const char*>(static_cast<const T*>(p.B1) + (int64_t)t.g * p.b_stride + t.n0);
+    } else {
+      Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)t.g * p.b_stride +
                                           (int64_t)t.n0 * ldb + kb0);
+      if (paired_epilogue(EPI))
+        Bub = reinterpret_cast<const char*>(static_cast<const T*>(p.B1) + (int64_t)t.g * p.b_stride +
+                                            (int64_t)t.n0 * ldb + kb0);
+    }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       // whether load step i reads A, gate or up is known at compile time
       const int byte = (i * NT + tid) * 16;
+      if constexpr (BKN) {
+        if (i >= CPA) {
+          // B along N: LDS chunk pc of k row kr holds columns 8 (pc ^ 4 (kr % 4)) .. + 7
+          const int ob = byte - BM * RB;
+          const int kr = ob / RBN;
+          const int col = min((((ob % RBN) / 16) ^ (4 * (kr % 4))) * 8, p.N - t.n0 - 8);  // past N: any valid
+          soff[i] = ((uint32_t)kr * (uint32_t)p.N + (uint32_t)col) * (uint32_t)sizeof(T);
+          continue;
+        }
+      }
       const int row = byte / RB;
       const int lc = Cfg::swz(row, (byte % RB) / 16);
       int r;
@@ -426,6 +471,19 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     if constexpr (STR) {
       const int64_t ks = row0 < BM ? p.ksa : p.ksb;
       if (ks) kstep = ks;
+    }
+    if constexpr (BKN) {
+      if (row0 >= BM) {
+        // k-slice kt is BK rows of B0, or of B1 past k_split
+        int ktb = kt;
+        const char* bb = Bgb;
+        if (p.k_split > 0 && kt * BK >= p.k_split) {
+          ktb = kt - p.k_split / BK;
+          bb = Bub;
+        }
+        lds_dma16(bb + (int64_t)ktb * BK * p.N * (int64_t)sizeof(T), soff[i], lbase + i * NT * 16);
+        return;
+      }
     }
     const int64_t kb = (int64_t)kt * kstep * (int64_t)sizeof(T);
     const char* base;
@@ -472,6 +530,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     }
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
+      if constexpr (BKN) {
+        // lane 4 j + m of each 16-lane group q points at k row kr + j, columns
+        // col .. col + 3; each lane then holds 4 consecutive k of one column, and the
+        // second read (4 rows further) completes the lane's 8 k values
+        const int q = lane >> 4, j = (lane >> 2) & 3;
+        const int kr = sub * 16 + 8 * (q >> 1) + j;
+        const int col = wn * Cfg::WTN + ni * 32 + 16 * (q & 1) + 4 * (lane & 3);
+        fb[buf % NBUF][ni] = read_tr16x2(sB + kr * RBN + (((col >> 3) ^ (4 * j)) << 4) + (col & 7) * 2, 4 * RBN);
+        continue;
+      }
       const int r = Cfg::b_row(wn, ni) + (lane & 31);
       if constexpr (Op::kReads == 1)
         Op::load(fb[buf % NBUF][ni], sB + r * RB + Cfg::swz(r, lc0) * 16);

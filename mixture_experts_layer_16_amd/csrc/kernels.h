@@ -45,8 +45,8 @@ hipError_t launch_newton_schulz(int64_t n, int64_t R, int64_t C, int64_t steps, 
 struct FfnBackwardScratch {
   int32_t* poff;   // [E+1] padded expert column offsets
   int32_t* pblk_expert;  // [n_pad / 64] expert of each 64-wide padded column block
-  void* wd_t;      // [E, F, d]   W_d transposed (I/O)
-  void* wgu_t;     // [E, d, 2F]  W_g and W_u transposed, side by side (I/O)
+  void* wd_t;      // [E, F, d]   W_d transposed (float32 layers only)
+  void* wgu_t;     // [E, d, 2F]  W_g and W_u transposed, side by side (float32 layers only)
   float* dh;       // [n_max, F]  dH (float32)
   void* dgu;       // [n_max, 2F] dG | dU (I/O)
   void* h;         // [n_max, F]  H recomputed (I/O)

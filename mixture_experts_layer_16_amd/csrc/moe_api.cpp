@@ -113,8 +113,9 @@ void carve_ffn_backward(Carver& c, moe::FfnBackwardScratch& w, int64_t n_max, in
   const int64_t n_pad = (n_max + 63 * E + 63) / 64 * 64;
   w.poff = static_cast<int32_t*>(c.take((size_t)(E + 1) * 4));
   w.pblk_expert = static_cast<int32_t*>(c.take((size_t)(n_pad / 64) * 4));
-  w.wd_t = c.take((size_t)E * F * d * es);
-  w.wgu_t = c.take((size_t)E * d * 2 * F * es);
+  // transposed weight copies: float32 only (16-bit weights are read in place)
+  w.wd_t = es == 4 ? c.take((size_t)E * F * d * es) : nullptr;
+  w.wgu_t = es == 4 ? c.take((size_t)E * d * 2 * F * es) : nullptr;
   w.dh = static_cast<float*>(c.take((size_t)n_max * F * 4));
   w.dgu = c.take((size_t)n_max * 2 * F * es);
   w.h = c.take((size_t)n_max * F * es);
