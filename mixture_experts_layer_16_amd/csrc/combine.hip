@@ -14,6 +14,21 @@ namespace moe {
 
 namespace {
 
+// 8 consecutive elements as one or two 16-byte loads, converted element by element.
+template <typename T> struct Raw16;
+template <> struct Raw16<bf16> {
+  typedef bf16x8 type;
+  __device__ __forceinline__ static type load(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ static float get(const type& v, int i) { return static_cast<float>(v[i]); }
+};
+template <> struct Raw16<float> {
+  struct type { f32x4 a, b; };
+  __device__ __forceinline__ static type load(const float* p) {
+    return {*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4)};
+  }
+  __device__ __forceinline__ static float get(const type& v, int i) { return i < 4 ? v.a[i] : v.b[i - 4]; }
+};
+
 // KU > 0: k is the compile-time KU, so the token's KU row loads are all in
 // flight before the first FMA; KU == 0: any k, in groups of 8.
 template <typename T, int KU>
@@ -33,21 +48,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_pe
       row[j] = __builtin_amdgcn_readfirstlane(sr[j]);
       wj[j] = wt[j];
     }
-    for (int c0 = lane * 8; c0 < d; c0 += 64 * 8) {
-      float v[KU][8];
-#pragma unroll
-      for (int j = 0; j < KU; ++j)
-        if (row[j] >= 0) load8(y_perm + (int64_t)row[j] * d + c0, v[j]);
-      float acc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    // two 512-column pieces per pass: 2 KU row loads in flight per lane
+    for (int c0 = lane * 8; c0 < d; c0 += 2 * 64 * 8) {
+      const int c1 = c0 + 64 * 8;
+      const bool has1 = c1 < d;
+      typename Raw16<T>::type v[2][KU];   // kept as loaded until the FMAs
 #pragma unroll
       for (int j = 0; j < KU; ++j)
         if (row[j] >= 0) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj[j], v[j][i], acc[i]);
+          v[0][j] = Raw16<T>::load(y_perm + (int64_t)row[j] * d + c0);
+          if (has1) v[1][j] = Raw16<T>::load(y_perm + (int64_t)row[j] * d + c1);
         }
-      store8(y + (int64_t)t * d + c0, acc);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < KU; ++j)
+          if (row[j] >= 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj[j], Raw16<T>::get(v[h][j], i), acc[i]);
+          }
+        if (h == 0) store8(y + (int64_t)t * d + c0, acc);
+        else if (has1) store8(y + (int64_t)t * d + c1, acc);
+      }
     }
   } else {
     for (int c0 = lane * 8; c0 < d; c0 += 64 * 8) {
