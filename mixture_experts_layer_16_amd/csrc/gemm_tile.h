@@ -351,6 +351,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   const int K = p.K;
   const int64_t lda = (STR && p.lda) ? p.lda : K, ldb = (STR && p.ldb) ? p.ldb : K;
   const T* __restrict__ Abase = static_cast<const T*>(p.A);
+  // B along N: bytes from one k-slice to the next; the first k-slice read from B1
+  // and the byte jump from B0's rows to B1's there
+  const uint32_t bkn_step = BKN ? (uint32_t)BK * (uint32_t)p.N * (uint32_t)sizeof(T) : 0u;
+  const int bkn_split = (BKN && p.k_split > 0) ? p.k_split / BK : 0x7fffffff;
+  const int64_t bkn_jump = (BKN && p.k_split > 0)
+                               ? (int64_t)((uintptr_t)p.B1 - (uintptr_t)p.B0) - (int64_t)bkn_split * bkn_step
+                               : 0;
 
   // ---- tile bookkeeping (all wave-uniform) ------------------------------------
   struct TileInfo {
@@ -426,8 +433,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     if constexpr (BKN) {
       // [K, N]: the tile's columns start n0 elements into every k row
       Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)t.g * p.b_stride + t.n0);
-      if (p.k_split > 0)
-        Bub = reinterpret_cast<const char*>(static_cast<const T*>(p.B1) + (int64_t)t.g * p.b_stride + t.n0);
     } else {
       Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)t.g * p.b_stride +
                                           (int64_t)t.n0 * ldb + kb0);
@@ -474,14 +479,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     }
     if constexpr (BKN) {
       if (row0 >= BM) {
-        // k-slice kt is BK rows of B0, or of B1 past k_split
-        int ktb = kt;
-        const char* bb = Bgb;
-        if (p.k_split > 0 && kt * BK >= p.k_split) {
-          ktb = kt - p.k_split / BK;
-          bb = Bub;
-        }
-        lds_dma16(bb + (int64_t)ktb * BK * p.N * (int64_t)sizeof(T), soff[i], lbase + i * NT * 16);
+        // k-slice kt is BK rows of B0, or of B1 past k_split (one base pointer
+        // and a fixed jump, so that only one pointer stays live)
+        lds_dma16(Bgb + (int64_t)kt * bkn_step + (kt >= bkn_split ? bkn_jump : 0), soff[i], lbase + i * NT * 16);
         return;
       }
     }
