@@ -203,7 +203,7 @@ def bench_newton_schulz(args, torch, B):
                    "tall": [n, d, F], "ns_steps": steps},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "moe_newton_schulz (3 batched GEMM launches + 1 transpose per step)",
+                     "kernel": "moe_newton_schulz (3 batched GEMM launches per step)",
                      "flops_per_launch": flops, "ms_per_launch": round(ms, 3)},
     }
     if args.cpu_tokens > 0:

@@ -301,7 +301,7 @@ moe_status moe_layer_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_
  *   steps              >= 0 (0: the normalised input)
  *   g   [n,R,C] bf16   input, row-major, matrices back to back
  *   x   [n,R,C] bf16   out, same layout; must not overlap g or ws
- *   ws: query with ws == NULL; about 3 n R C + 2 n min(R,C)^2 bf16 elements.
+ *   ws: query with ws == NULL; about 2 n R C + 2 n min(R,C)^2 bf16 elements.
  * Errors: n, R, C <= 0, steps < 0 or eps < 0 or NaN: MOE_ERR_INVALID_ARG;
  * R or C not a multiple of 64, dtype not bf16, sizes past the limits:
  * MOE_ERR_UNSUPPORTED; g, x, ws not 16-byte aligned: MOE_ERR_INVALID_ARG.

@@ -33,12 +33,12 @@ hipError_t launch_grouped_ffn(int dtype, int64_t n_max, int64_t d, int64_t E, in
                               int num_cu, hipStream_t stream);
 
 // Muon's Newton-Schulz orthogonalisation of n bf16 matrices [R, C] (R, C multiples
-// of 64): g in, x out; xw [n, R', C'], xt0 and xt1 [n, C', R'], A and B [n, R', R']
+// of 64): g in, x out; xw0 and xw1 [n, R', C'], A and B [n, R', R']
 // (R' = min(R, C), C' = max(R, C)) and partial [n * kNormBlocks] are scratch.
 constexpr int kNormBlocks = 64;
 hipError_t launch_newton_schulz(int64_t n, int64_t R, int64_t C, int64_t steps, float a, float b, float c,
-                                float eps, const void* g, void* x, void* xw, void* xt0, void* xt1, void* A,
-                                void* B, float* partial, int num_cu, hipStream_t stream);
+                                float eps, const void* g, void* x, void* xw0, void* xw1, void* A, void* B,
+                                float* partial, int num_cu, hipStream_t stream);
 
 // Backward of the grouped SwiGLU FFN: dx_perm and the float32 weight gradients
 // from dy_perm.  Scratch (caller-carved; "I/O" = the dtype's element type):

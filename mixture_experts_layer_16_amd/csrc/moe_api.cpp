@@ -378,8 +378,7 @@ moe_status moe_newton_schulz(int64_t n, int64_t R, int64_t C, moe_dtype dtype, i
     return MOE_ERR_UNSUPPORTED;
   const size_t per = (size_t)R * (size_t)C * 2, sq = (size_t)(R < C ? R : C) * (size_t)(R < C ? R : C) * 2;
   Carver c0(nullptr);
-  c0.take(n * per);                               // X, wide orientation
-  c0.take(n * per);                               // X^T, two of them
+  c0.take(n * per);                               // X, wide orientation, two of them
   c0.take(n * per);
   c0.take(n * sq);                                // A = X X^T
   c0.take(n * sq);                                // B = b A + c A A
@@ -395,13 +394,12 @@ moe_status moe_newton_schulz(int64_t n, int64_t R, int64_t C, moe_dtype dtype, i
   int ncu = 0;
   if ((st = num_cu(&ncu)) != MOE_OK) return st;
   Carver cv(ws);
-  void* xw = cv.take(n * per);
-  void* xt0 = cv.take(n * per);
-  void* xt1 = cv.take(n * per);
+  void* xw0 = cv.take(n * per);
+  void* xw1 = cv.take(n * per);
   void* A = cv.take(n * sq);
   void* B = cv.take(n * sq);
   float* partial = static_cast<float*>(cv.take((size_t)n * moe::kNormBlocks * 4));
-  return hip_status(moe::launch_newton_schulz(n, R, C, steps, a, b, c, eps, g, x, xw, xt0, xt1, A, B, partial, ncu,
+  return hip_status(moe::launch_newton_schulz(n, R, C, steps, a, b, c, eps, g, x, xw0, xw1, A, B, partial, ncu,
                                               static_cast<hipStream_t>(stream)));
 }
 

@@ -13,16 +13,15 @@
 //   * sum of squares per matrix: kNormBlocks partial sums, each over a fixed
 //     contiguous chunk, then every consumer adds the partials in one fixed order
 //     (deterministic, no atomics);
-//   * init: X0 scaled and cast, written both as Xw [R', C'] (wide) and as its
-//     transpose Xt [C', R'] through a 64 x 64 LDS tile;
-//   * per step, three launches of the grouped NT GEMM with one group per matrix:
-//       A  = Xw Xw^T                   (K = C')
-//       B  = c (A A^T) + b A           (K = R'; A is symmetric, so A A^T = A A)
-//       Xt' = (Xt B^T) + a Xt          (K = R'; B is symmetric, so Xt B^T = (B Xw)^T)
-//     then Xt' is transposed back into Xw for the next step's A (the product
-//     forms of the GEMM read both operands along K, so X X^T needs X's rows and
-//     B X needs X^T's rows).  The last step writes the result in the caller's
-//     orientation straight into the output.
+//   * init: X0 scaled and cast, written in the wide orientation Xw [R', C'] (a
+//     tall G through a 64 x 64 LDS tile);
+//   * per step, three launches of the grouped GEMM with one group per matrix:
+//       A   = Xw Xw^T              (NT, K = C')
+//       B   = c (A A^T) + b A      (NT, K = R'; A is symmetric, so A A^T = A A)
+//       Xw' = B Xw + a Xw          (K = R'; Xw is read where it lies, as a B
+//                                   operand stored along N), into the other Xw
+//     A wide matrix's last step writes the caller's output directly; a tall
+//     one's result is transposed once at the end.
 #include "common.h"
 #include "gemm_tile.h"
 #include "kernels.h"
@@ -58,7 +57,8 @@ __global__ __launch_bounds__(256) void ns_sumsq_kernel(const bf16* __restrict__ 
 }
 
 // scale = 1 / (sqrt(sum of the partials in order) + eps); out_same = scale * G (G's
-// orientation), out_t = its transpose, both rounded once to bf16.  One 64 x 64 tile
+// orientation), out_t = its transpose, both rounded once to bf16 (either may be
+// null: not written).  One 64 x 64 tile
 // of one matrix per block: each thread reads 16 consecutive elements of one row
 // (two 16-byte loads), writes them scaled in place order, and parks them in LDS
 // column-wise; then reads 16 consecutive elements of one transposed row.
@@ -91,8 +91,11 @@ __global__ __launch_bounds__(256) void ns_init_kernel(const bf16* __restrict__ g
       tile[q + 8 * h + 2 * e + 1][r] = (uint16_t)(w[e] >> 16);
     }
   }
-  *reinterpret_cast<bf16x8*>(out_same + off) = v[0];
-  *reinterpret_cast<bf16x8*>(out_same + off + 8) = v[1];
+  if (out_same) {
+    *reinterpret_cast<bf16x8*>(out_same + off) = v[0];
+    *reinterpret_cast<bf16x8*>(out_same + off + 8) = v[1];
+  }
+  if (out_t == nullptr) return;   // (the same for the whole block)
   __syncthreads();
   const int c = t >> 2, p = (t & 3) * 16;
   const uint32_t* row = reinterpret_cast<const uint32_t*>(&tile[c][0]) + p / 2;
@@ -144,22 +147,21 @@ GemmArgs batch_gemm(const bf16* A, const bf16* B, int64_t b_stride, int n, int64
 }  // namespace
 
 hipError_t launch_newton_schulz(int64_t n, int64_t R, int64_t C, int64_t steps, float a, float b, float c,
-                                float eps, const void* g, void* x, void* xw, void* xt0, void* xt1, void* A,
-                                void* B, float* partial, int num_cu, hipStream_t stream) {
+                                float eps, const void* g, void* x, void* xw0, void* xw1, void* A, void* B,
+                                float* partial, int num_cu, hipStream_t stream) {
   const bool tall = R > C;
   const int64_t Rw = tall ? C : R, Cw = tall ? R : C;   // wide orientation
   const int64_t per = R * C;
   const bf16* G = static_cast<const bf16*>(g);
   bf16* X = static_cast<bf16*>(x);
-  bf16* Xw = static_cast<bf16*>(xw);
-  bf16* Xt[2] = {static_cast<bf16*>(xt0), static_cast<bf16*>(xt1)};
+  bf16* Xw[2] = {static_cast<bf16*>(xw0), static_cast<bf16*>(xw1)};
   bf16* Ab = static_cast<bf16*>(A);
   bf16* Bb = static_cast<bf16*>(B);
 
   hipLaunchKernelGGL(ns_sumsq_kernel, dim3(kNormBlocks, (unsigned)n), dim3(256), 0, stream, G, per, partial);
-  // X0 in G's orientation and transposed; which one is the wide one depends on tall
-  bf16* same = steps == 0 ? X : (tall ? Xt[0] : Xw);
-  bf16* trans = tall ? Xw : Xt[0];
+  // X0: the output itself when there are no steps, else the wide orientation
+  bf16* same = steps == 0 ? X : (tall ? nullptr : Xw[0]);
+  bf16* trans = (steps == 0 || !tall) ? nullptr : Xw[0];
   hipLaunchKernelGGL(ns_init_kernel, dim3((unsigned)(C / kTile), (unsigned)(R / kTile), (unsigned)n), dim3(256), 0,
                      stream, G, (int)R, (int)C, partial, eps, same, trans);
   if (steps == 0) return hipGetLastError();
@@ -169,7 +171,7 @@ hipError_t launch_newton_schulz(int64_t n, int64_t R, int64_t C, int64_t steps, 
   for (int64_t s = 0; s < steps; ++s) {
     const bool last = s + 1 == steps;
     // A = Xw Xw^T
-    GemmArgs p1 = batch_gemm(Xw, Xw, Rw * Cw, (int)n, Rw, (int)Rw, (int)Cw, Ab);
+    GemmArgs p1 = batch_gemm(Xw[cur], Xw[cur], Rw * Cw, (int)n, Rw, (int)Rw, (int)Cw, Ab);
     hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, BK, WM, WN, ST, EPI_STORE, 1, kFeatGroups>), dim3(num_cu),
                        dim3(WM * WN * 64), 0, stream, p1);
     // B = c (A A^T) + b A
@@ -179,20 +181,21 @@ hipError_t launch_newton_schulz(int64_t n, int64_t R, int64_t C, int64_t steps, 
     p2.D = Ab;
     hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, BK, WM, WN, ST, EPI_AXPBY, 1, kFeatGroups>), dim3(num_cu),
                        dim3(WM * WN * 64), 0, stream, p2);
-    // Xt' = Xt B^T + a Xt; for a tall matrix Xt is the caller's orientation
-    bf16* out = (last && tall) ? X : Xt[cur ^ 1];
-    GemmArgs p3 = batch_gemm(Xt[cur], Bb, Rw * Rw, (int)n, Cw, (int)Rw, (int)Rw, out);
+    // Xw' = B Xw + a Xw (Xw [R', C'] read along C' as stored); a wide matrix's last
+    // step writes the caller's output
+    bf16* out = (last && !tall) ? X : Xw[cur ^ 1];
+    GemmArgs p3 = batch_gemm(Bb, Xw[cur], Rw * Cw, (int)n, Rw, (int)Cw, (int)Rw, out);
     p3.alpha = 1.0f;
     p3.beta = a;
-    p3.D = Xt[cur];
-    hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, BK, WM, WN, ST, EPI_AXPBY, 1, kFeatGroups>), dim3(num_cu),
-                       dim3(WM * WN * 64), 0, stream, p3);
-    if (last && tall) break;
-    // Xw = Xt'^T (the result itself on the last step of a wide matrix)
-    hipLaunchKernelGGL(ns_transpose_kernel, dim3((unsigned)(Rw / kTile), (unsigned)(Cw / kTile), (unsigned)n),
-                       dim3(256), 0, stream, out, (int)Cw, (int)Rw, last ? X : Xw);
+    p3.D = Xw[cur];
+    hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, BK, WM, WN, ST, EPI_AXPBY, 1, kFeatGroups | kFeatBKN>),
+                       dim3(num_cu), dim3(WM * WN * 64), 0, stream, p3);
     cur ^= 1;
   }
+  // a tall matrix: its result is the transpose of the wide one
+  if (tall)
+    hipLaunchKernelGGL(ns_transpose_kernel, dim3((unsigned)(Cw / kTile), (unsigned)(Rw / kTile), (unsigned)n),
+                       dim3(256), 0, stream, Xw[cur], (int)Rw, (int)Cw, X);
   return hipGetLastError();
 }
 

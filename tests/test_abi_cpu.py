@@ -197,7 +197,7 @@ def ns(n=2, R=128, C=192, dt=1, steps=5, eps=1e-7, g=P, x=P, ws=P, nbytes=1 << 3
 
 def ns_ws(n, R, C):
     per, sq = R * C * 2, min(R, C) ** 2 * 2
-    return 3 * ru(n * per) + 2 * ru(n * sq) + ru(n * 64 * 4)
+    return 2 * ru(n * per) + 2 * ru(n * sq) + ru(n * 64 * 4)
 
 
 @pytest.mark.parametrize("n,R,C", [(1, 64, 64), (3, 128, 320), (2, 320, 128), (288, 1792, 6144)])
