@@ -5,9 +5,11 @@
 // matrices with a fused SwiGLU epilogue) and the expert down GEMM.
 //
 // Design (CDNA4):
-//  * a workgroup of WM x WN waves owns a BM x BN output tile; each wave owns a
-//    (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA blocks whose float32
-//    accumulators stay in registers for the whole K loop;
+//  * a workgroup of WM x WN waves owns a BM x BN output tile; each wave owns
+//    BM/WM rows (the 32-row blocks wm, wm + WM, wm + 2 WM, ...) and BN/WN
+//    columns, as 32x32 MFMA blocks whose float32 accumulators stay in registers
+//    for the whole K loop.  Interleaving the row blocks keeps a ragged tile's
+//    live rows spread evenly over the SIMDs (waves w and w + 4 share a SIMD);
 //  * A and B k-slices travel global -> LDS with the gfx950 16-byte direct-to-LDS
 //    load (no register staging), STAGES deep; each LDS row holds BK elements
 //    (64 or 128 bytes) with its 16-byte chunks XOR-swizzled by row so that the
@@ -503,7 +505,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   };
 
   // Row blocks past the end of a ragged row tile carry no output: their MFMAs and
-  // A-fragment reads are skipped (mi_live is wave-uniform).
+  // A-fragment reads are skipped (mi_live is wave-uniform).  With this wave's
+  // blocks wm + WM mi, a tile with r live blocks leaves each SIMD at most
+  // ceil(r / 2) of them (contiguous blocks per wave: up to 4 for r = 6).
   int mi_live = MI;
 
   // ---- MFMA operand fragments: one buffer per sub-step of a k-tile, read PD
@@ -522,7 +526,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
       if (!full && mi >= mi_live) continue;
-      const int r = wm * Cfg::WTM + mi * 32 + (lane & 31);
+      const int r = (wm + WM * mi) * 32 + (lane & 31);
       if constexpr (Op::kReads == 1)
         Op::load(fa[buf % NBUF][mi], sA + r * RB + Cfg::swz(r, lc0) * 16);
       else
@@ -605,9 +609,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
       static_assert(CW % RC == 0, "whole rounds");
       char* wlane = wbuf + (lane & 31) * RS + h4 * ES;                     // this lane's row and column offset
       const char* rlane = wbuf + (lane >> 3) * RS + (lane & 7) * 16;
-      // read-back rows r0 + 32 mi + 8 it of this wave; one 64-bit address per lane,
-      // stepped by scalars (no per-row 64-bit products to keep live)
-      const int r0 = wm * Cfg::WTM + (lane >> 3);
+      // read-back rows r0 + 32 WM mi + 8 it of this wave (its row blocks are
+      // wm + WM mi); one 64-bit address per lane, stepped by scalars (no per-row
+      // 64-bit products to keep live)
+      const int r0 = wm * 32 + (lane >> 3);
       const int rrem = erows - r0;
       const int c0l = en0 + wn * CW + (lane & 7) * (16 / ES);
       OT* cbase = static_cast<OT*>(dstp) + (em0 + r0) * ld + c0l;
@@ -635,8 +640,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
             const int cc = c0l + rd * RC;
             if constexpr (f32_epilogue(EPI)) {
               // N need not be a multiple of 4 here (a router's expert count)
-              if (mi * 32 + it * 8 < rrem) {
-                OT* dst = cbase + (4 * mi + it) * rstep + rd * RC;
+              if (mi * 32 * WM + it * 8 < rrem) {
+                OT* dst = cbase + (4 * WM * mi + it) * rstep + rd * RC;
                 if (cc + 16 / ES <= p.N) {
                   *reinterpret_cast<u32x4*>(dst) = piece;
                 } else if (cc < p.N) {
@@ -645,8 +650,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
                 }
               }
             } else {
-              if (mi * 32 + it * 8 < rrem && cc < p.N)
-                *reinterpret_cast<u32x4*>(cbase + (4 * mi + it) * rstep + rd * RC) = piece;
+              if (mi * 32 * WM + it * 8 < rrem && cc < p.N)
+                *reinterpret_cast<u32x4*>(cbase + (4 * WM * mi + it) * rstep + rd * RC) = piece;
             }
           }
           wait_lgkmcnt0();
@@ -681,7 +686,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
       const int64_t ldc = (EPI == EPI_SWIGLU_BWD && p.ldc) ? p.ldc : p.N;
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
-        const int r = wm * Cfg::WTM + mi * 32 + (lane & 31);
+        const int r = (wm + WM * mi) * 32 + (lane & 31);
         if (r >= erows) continue;               // (lanes l and l + 32 share the row)
         T* crow = static_cast<T*>(p.C) + (em0 + r) * ldc;
 #pragma unroll
@@ -809,7 +814,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.f;
 
-    mi_live = __builtin_amdgcn_readfirstlane(min(MI, max(0, (cur.rows_valid - wm * Cfg::WTM + 31) / 32)));
+    {
+      // row blocks with a valid row; this wave's are blocks wm + WM mi
+      const int nb = (cur.rows_valid + 31) / 32;
+      mi_live = __builtin_amdgcn_readfirstlane(nb > wm ? min(MI, (nb - wm + WM - 1) / WM) : 0);
+    }
 
     // k-tile 0 has landed (this wave's copies; the barrier covers the others)
     if (STAGES - 2 <= nk - 1) wait_vmcnt<(STAGES - 2) * CPT>();
