@@ -257,23 +257,28 @@ def test_k_and_E_extremes(T, E, k):
         assert np.all(f64(L.topk_w) == 1.0)
 
 
-def test_equal_logits_pick_lowest_indices():
-    wl = W.Workload("ties", T=200, d=128, E=12, k=3, F=64, dtype=torch.bfloat16)
+# (E, k) reach both top-k kernels: one wavefront per token (E <= 64, or k > 16) and
+# one 16-lane row per token (E a multiple of 4 in (64, 512], k <= 16)
+@pytest.mark.parametrize("E,k", [(12, 3), (384, 8), (128, 16), (384, 17)])
+def test_equal_logits_pick_lowest_indices(E, k):
+    print(f"[ties] E={E} k={k}", flush=True)
+    wl = W.Workload("ties", T=200, d=128, E=E, k=k, F=64, dtype=torch.bfloat16)
     inp = _inputs(wl)
     inp["w_router"].zero_()
     L, _ = _layer_vs_oracle(inp, wl)
-    assert np.array_equal(i64(L.topk_ids), np.broadcast_to(np.arange(3), (200, 3)))
-    assert np.abs(f64(L.topk_w) - 1.0 / 3.0).max() <= 1e-6
+    assert np.array_equal(i64(L.topk_ids), np.broadcast_to(np.arange(k), (200, k)))
+    assert np.abs(f64(L.topk_w) - 1.0 / k).max() <= 1e-6
 
 
-def test_identity_router_crafts_exact_ties():
+@pytest.mark.parametrize("E,k,T", [(64, 5, 256), (128, 8, 256), (384, 8, 250), (384, 16, 250)])
+def test_identity_router_crafts_exact_ties(E, k, T):
     # d == E and W_r = I: the logits are x itself (one exact product per dot
     # product), so crafted equal values (and -0.0 vs +0.0) are exact ties.
-    E = 64
-    wl = W.Workload("eye", T=256, d=E, E=E, k=5, F=64, dtype=torch.bfloat16)
+    print(f"[eye] E={E} k={k} T={T}", flush=True)
+    wl = W.Workload("eye", T=T, d=E, E=E, k=k, F=64, dtype=torch.bfloat16)
     inp = _inputs(wl)
-    r = np.random.default_rng(21)
-    vals = r.choice(np.array([-1.0, -0.0, 0.0, 0.5, 0.5, 1.0, 2.0], dtype=np.float32), size=(256, E))
+    r = np.random.default_rng(21 + E + k)
+    vals = r.choice(np.array([-1.0, -0.0, 0.0, 0.5, 0.5, 1.0, 2.0], dtype=np.float32), size=(T, E))
     inp["x"] = torch.from_numpy(vals).to(DEV).to(torch.bfloat16)
     inp["w_router"] = torch.eye(E, device=DEV, dtype=torch.bfloat16)
     L, _ = _layer_vs_oracle(inp, wl)
