@@ -848,8 +848,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
             read_frags(FULL, s + PD, st, s + PD);
           } else {
             // every LDS read of stage st has been issued: wait for them (on every
-            // path, so the compiler sees one state after the branch)
-            if constexpr (s + PD == KSUB) wait_lgkmcnt0();
+            // path, so the compiler sees one state after the branch).  The
+            // scheduling barrier keeps the previous sub-step's MFMAs above the wait:
+            // they touch no memory, and the compiler otherwise sinks them below it,
+            // exposing the latency of the reads just issued once per k-tile.
+            if constexpr (s + PD == KSUB) {
+              __builtin_amdgcn_sched_barrier(0);
+              wait_lgkmcnt0();
+            }
             if (kt + 1 < nk) {
               if constexpr (s + PD == KSUB) {
                 // k-tile kt+1 has landed: recycle stage st for k-tile kt+STAGES
