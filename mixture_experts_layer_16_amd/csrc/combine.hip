@@ -14,21 +14,6 @@ namespace moe {
 
 namespace {
 
-// 8 consecutive elements as one or two 16-byte loads, converted element by element.
-template <typename T> struct Raw16;
-template <> struct Raw16<bf16> {
-  typedef bf16x8 type;
-  __device__ __forceinline__ static type load(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
-  __device__ __forceinline__ static float get(const type& v, int i) { return static_cast<float>(v[i]); }
-};
-template <> struct Raw16<float> {
-  struct type { f32x4 a, b; };
-  __device__ __forceinline__ static type load(const float* p) {
-    return {*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4)};
-  }
-  __device__ __forceinline__ static float get(const type& v, int i) { return i < 4 ? v.a[i] : v.b[i - 4]; }
-};
-
 // KU > 0: k is the compile-time KU, so the token's KU row loads are all in
 // flight before the first FMA; KU == 0: any k, in groups of 8.
 template <typename T, int KU>

@@ -148,23 +148,24 @@ __global__ __launch_bounds__(256) void route_backward_token_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     if constexpr (KU > 0) {
-      float v[KU][8], r[KU][8];
+      // rows kept as loaded until used (half the registers of float copies)
+      typename Raw16<T>::type v[KU], r[KU];
 #pragma unroll
       for (int j = 0; j < KU; ++j) {
-        if (row[j] >= 0) load8(dx_perm + (int64_t)row[j] * d + c0, v[j]);
-        if (id[j] >= 0) load8(w_router + (int64_t)id[j] * d + c0, r[j]);
+        if (row[j] >= 0) v[j] = Raw16<T>::load(dx_perm + (int64_t)row[j] * d + c0);
+        if (id[j] >= 0) r[j] = Raw16<T>::load(w_router + (int64_t)id[j] * d + c0);
       }
 #pragma unroll
       for (int j = 0; j < KU; ++j)
         if (row[j] >= 0) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] += v[j][i];
+          for (int i = 0; i < 8; ++i) acc[i] += Raw16<T>::get(v[j], i);
         }
 #pragma unroll
       for (int j = 0; j < KU; ++j)
         if (id[j] >= 0) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] = fmaf(dl[j], r[j][i], acc[i]);
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(dl[j], Raw16<T>::get(r[j], i), acc[i]);
         }
     } else {
       float v[8];

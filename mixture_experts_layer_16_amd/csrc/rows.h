@@ -7,6 +7,23 @@
 
 namespace moe {
 
+// 8 consecutive elements kept as loaded (one or two 16-byte loads) and converted
+// element by element where they are used: half the registers of a float32 copy
+// for 16-bit rows, so more row loads fit in flight.
+template <typename T> struct Raw16;
+template <> struct Raw16<bf16> {
+  typedef bf16x8 type;
+  __device__ __forceinline__ static type load(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ static float get(const type& v, int i) { return static_cast<float>(v[i]); }
+};
+template <> struct Raw16<float> {
+  struct type { f32x4 a, b; };
+  __device__ __forceinline__ static type load(const float* p) {
+    return {*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4)};
+  }
+  __device__ __forceinline__ static float get(const type& v, int i) { return i < 4 ? v.a[i] : v.b[i - 4]; }
+};
+
 __device__ __forceinline__ void load8(const bf16* p, float* v) {
   const bf16x8 q = *reinterpret_cast<const bf16x8*>(p);
 #pragma unroll
