@@ -365,14 +365,16 @@ def main():
         L()
     torch.cuda.synchronize()
 
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps (no synchronisation inside the timed region)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
+    evs[0].record()
+    for i in range(args.steps):
         L()
-    end.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     tokens_per_s = wl.T / (ms / 1e3)
 
     stages = stage_pass(torch, B, inp, wl, max(2, min(args.steps, 5)))
@@ -399,6 +401,7 @@ def main():
                      "kernel": "grouped SwiGLU FFN (gate/up + down GEMM launches)",
                      "flops_per_launch": wl.expert_flops(), "ms_per_launch": round(ffn_ms, 4)},
         "tflops_layer": round(total_tflops, 1),
+        "step_ms": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4)},
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "hbm_frac": {"permute": round(perm_bytes / (stages["permute"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
                      "combine": round(comb_bytes / (stages["combine"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)},
