@@ -339,8 +339,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the layer's expert-parallel sharding is described in DESIGN.md).", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(expert-parallel sharding of the layer is a design, not code).", file=sys.stderr)
         sys.exit(2)
 
     import torch
