@@ -249,7 +249,8 @@ def _layer_vs_oracle(inp, wl):
     return L, ref
 
 
-@pytest.mark.parametrize("T,E,k", [(300, 16, 1), (300, 8, 8), (300, 1, 1), (1, 4, 2), (16, 64, 2)])
+@pytest.mark.parametrize("T,E,k", [(300, 16, 1), (300, 8, 8), (300, 1, 1), (1, 4, 2), (16, 64, 2),
+                                   (5, 384, 8), (1, 512, 16), (33, 256, 4)])
 def test_k_and_E_extremes(T, E, k):
     wl = W.Workload("edge", T=T, d=128, E=E, k=k, F=128, dtype=torch.bfloat16)
     L, ref = _layer_vs_oracle(_inputs(wl, seed=T + E + k), wl)
@@ -270,7 +271,8 @@ def test_equal_logits_pick_lowest_indices(E, k):
     assert np.abs(f64(L.topk_w) - 1.0 / k).max() <= 1e-6
 
 
-@pytest.mark.parametrize("E,k,T", [(64, 5, 256), (128, 8, 256), (384, 8, 250), (384, 16, 250)])
+@pytest.mark.parametrize("E,k,T", [(64, 5, 256), (128, 8, 256), (384, 8, 250), (384, 16, 250), (512, 16, 70),
+                                   (256, 3, 100)])
 def test_identity_router_crafts_exact_ties(E, k, T):
     # d == E and W_r = I: the logits are x itself (one exact product per dot
     # product), so crafted equal values (and -0.0 vs +0.0) are exact ties.
