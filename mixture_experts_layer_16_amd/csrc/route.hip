@@ -232,7 +232,12 @@ hipError_t launch_router_gemm(int dtype, int64_t T, int64_t d, int64_t E, const 
   a.n_group = 0;
   a.m_chunk = 0;
   const dim3 grid((unsigned)num_cu), block(512);
-  if (dtype == 1)
+  // bf16: the tile width of 192 or 256 columns that pads E less (E = 384 fits two
+  // 192-wide tiles exactly, where 256-wide tiles would compute 512 columns)
+  const bool narrow = (E + 191) / 192 * 192 < (E + 255) / 256 * 256;
+  if (dtype == 1 && narrow)
+    hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 192, 64, 4, 2, 2, EPI_F32_BIAS>), grid, block, 0, stream, a);
+  else if (dtype == 1)
     hipLaunchKernelGGL((grouped_gemm_kernel<bf16, 256, 256, 64, 4, 2, 2, EPI_F32_BIAS>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((grouped_gemm_kernel<float, 256, 256, 32, 4, 2, 2, EPI_F32_BIAS>), grid, block, 0, stream, a);
