@@ -382,8 +382,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
       local = tile - __builtin_amdgcn_readfirstlane(tstart[t.g]);
     }
     const int64_t grows = GRP ? p.group_rows : 0;
-    const int64_t seg_lo = p.seg ? (int64_t)p.seg[t.g] : (int64_t)t.g * grows;
-    const int64_t seg_hi = p.seg ? (int64_t)p.seg[t.g + 1] : (grows > 0 ? seg_lo + grows : p.M);
+    // offsets are read-only here: read them through the scalar cache
+    const int32_t __attribute__((address_space(4)))* sseg =
+        (const int32_t __attribute__((address_space(4)))*)p.seg;
+    const int64_t seg_lo = p.seg ? (int64_t)sseg[t.g] : (int64_t)t.g * grows;
+    const int64_t seg_hi = p.seg ? (int64_t)sseg[t.g + 1] : (grows > 0 ? seg_lo + grows : p.M);
     // Within a group the tiles run in chunks of SM row tiles; inside a chunk, in
     // column groups of NG column tiles; inside a column group, row tile by row
     // tile.  Consecutive tiles then share A rows (same row tile) and B columns
@@ -824,14 +827,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     if (STAGES - 2 <= nk - 1) wait_vmcnt<(STAGES - 2) * CPT>();
     else wait_vmcnt<0>();
     block_barrier();
-    if (STAGES - 1 < nk) load_stage((STAGES - 1) % STAGES, STAGES - 1);
-    // look up the next tile now; its row numbers arrive during this K loop
+    // look up the next tile now, before the next stage's copies go out: the
+    // compiler waits for its own loads with a full memory-counter wait, which
+    // would also wait for copies issued ahead of them.  Its row numbers arrive
+    // during this K loop.
     const int next_tile = tile + step;
     const bool more = next_tile < end;
     if (more) {
       nxt = locate(next_tile);
       fetch_rows(nxt, arow_n);
     }
+    if (STAGES - 1 < nk) load_stage((STAGES - 1) % STAGES, STAGES - 1);
       // the K loop, compiled twice: without per-block checks for tiles whose row
     // blocks are all live, with them for ragged tiles (the checks cost the
     // compiler its exact tracking of outstanding LDS reads)
