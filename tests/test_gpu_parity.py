@@ -249,8 +249,11 @@ def _layer_vs_oracle(inp, wl):
     return L, ref
 
 
+# E also spans both router tile widths (192 columns where that pads E less than
+# 256: E = 192, 384, 576; 256 otherwise: E = 196, 256, 512) and E > 512
 @pytest.mark.parametrize("T,E,k", [(300, 16, 1), (300, 8, 8), (300, 1, 1), (1, 4, 2), (16, 64, 2),
-                                   (5, 384, 8), (1, 512, 16), (33, 256, 4)])
+                                   (5, 384, 8), (1, 512, 16), (33, 256, 4), (300, 192, 6), (260, 196, 8),
+                                   (77, 576, 8)])
 def test_k_and_E_extremes(T, E, k):
     wl = W.Workload("edge", T=T, d=128, E=E, k=k, F=128, dtype=torch.bfloat16)
     L, ref = _layer_vs_oracle(_inputs(wl, seed=T + E + k), wl)
