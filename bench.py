@@ -62,7 +62,7 @@ def parse():
 # of the page shape, from rocprofv3 FETCH_SIZE and WRITE_SIZE runs of
 # `bench.py --traffic-probe`, each scaled by the same counter's reading for a
 # 1 GiB device copy.  Valid only for the kernel sources it was measured on.
-TRAFFIC = {"workload": "page_seq64k_skewed", "kernel_source_hash": "92e61465bac221b9", "bytes": 103707244009,
+TRAFFIC = {"workload": "page_seq64k_skewed", "kernel_source_hash": "11923f4b7f7d288c", "bytes": 103722648169,
            "fetch_scale": 1.9999, "write_scale": 1.0000}
 KERNEL_SOURCES = ["mixture_experts_layer_16_amd/csrc/gemm_tile.h", "mixture_experts_layer_16_amd/csrc/grouped_ffn.hip",
                   "mixture_experts_layer_16_amd/csrc/common.h"]

@@ -570,15 +570,20 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   auto mma_all_copy = [&](auto j0c, auto j1c, bool full, int buf, int stage, int kt, bool copy) {
     constexpr int J0 = decltype(j0c)::value, J1 = decltype(j1c)::value;
     constexpr int NM = MI * NI, NJ = J1 - J0;
+    // the copies are spread over the first half of the MFMAs (after MFMA q for
+    // q < NF, with q * NJ / NF stepping up): earlier than spread over all of
+    // them, so each gets more cover, but not in one burst.  Measured on the
+    // page-shape grouped FFN: 1.6% faster than all MFMAs, 0.4-1.6% faster than
+    // the first quarter
+    constexpr int NF = NM > 1 ? NM / 2 : 1;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         if (full || mi < mi_live) Op::mma(fb[buf % NBUF][ni], fa[buf % NBUF][mi], acc[mi][ni]);
         const int q = mi * NI + ni;
-        // copies go after MFMAs q with q * NJ / NM stepping up
 #pragma unroll
-        for (int j = J0 + q * NJ / NM; j < J0 + (q + 1) * NJ / NM; ++j)
+        for (int j = J0 + min(q, NF) * NJ / NF; j < J0 + min(q + 1, NF) * NJ / NF; ++j)
           if (copy) load_one(stage, kt, j);
       }
   };
