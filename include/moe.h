@@ -68,6 +68,10 @@ typedef enum moe_status {
 
 /*
  * moe_route: router GEMM, softmax and top-k (first two steps of the layer).
+ * Passage: the model-configuration table in the TL;DR of "Training a
+ * 1T-Parameter MoE on EU public infrastructure with PyTorch and TorchTitan"
+ * (384 routed experts, each token uses the top 8); the score function (softmax
+ * over all routed experts), the tie rule and the renormalisation are readings.
  *   x          [T,d]  dtype      input tokens
  *   w_router   [E,d]  dtype      router weights
  *   bias       [E]    float32    per-expert routing bias added to the logits, or NULL
@@ -83,10 +87,17 @@ moe_status moe_route(int64_t T, int64_t d, int64_t E, int64_t k, moe_dtype dtype
 
 /*
  * moe_permute: group the (token, slot) pairs by expert and copy token rows.
+ * Passage: section 二 of "Domyn 团队在 Jupiter 超算完成 1 万亿参数 MoE 模型训练项目解析"
+ * (each token is routed to a few expert sub-networks, so each expert's rows must
+ * be gathered); dropless routing as on the Pangu Ultra MoE page (every slot gets
+ * a row, no capacity limit).  The result is the stable counting sort of the slots
+ * taken token by token, slot by slot.
  *   x          [T,d]   dtype     input tokens
  *   topk_ids   [T,k]   int32     expert of each slot; a negative id (or one >= E)
  *                                 marks a slot whose expert is not on this GPU: it
- *                                 is skipped.  The ids of one token must be distinct.
+ *                                 is skipped.  A token naming the same expert in
+ *                                 several slots (top-k never does) gets one row per
+ *                                 slot, in slot order, like any other slot.
  *   offsets    [E+1]   int32     out: rows offsets[e]..offsets[e+1]-1 belong to expert e;
  *                                 offsets[E] = number of valid slots N
  *   row_token  [T*k]   int32     out: row r copies token row_token[r]; rows of one
@@ -104,15 +115,25 @@ moe_status moe_permute(int64_t T, int64_t d, int64_t E, int64_t k, moe_dtype dty
 
 /*
  * moe_grouped_ffn: the SwiGLU FFN of every expert over its own rows.
- *   n_max              capacity (rows) of y_perm (and of x_in without a_rows);
- *                       offsets[E] <= n_max is the caller's promise (the row count
- *                       is read on the device; nothing is copied back)
+ * Passage: the model-configuration table of "Training a 1T-Parameter MoE on EU
+ * public infrastructure with PyTorch and TorchTitan" (hidden 6,144, expert hidden
+ * 1,792; its parameter counts fit three d x F matrices per expert, a gated FFN);
+ * SwiGLU is the reading of the gate.
+ *   n_max              capacity (rows) of y_perm (and of x_in without a_rows)
+ *   offsets are read on the device (nothing is copied back) and are not trusted:
+ *                       the kernels use the running maximum of offsets[0..e],
+ *                       clamped to [0, n_max], as expert e's first row.  Offsets
+ *                       as moe_permute writes them (non-decreasing, offsets[E] <=
+ *                       n_max) pass through unchanged; any others give unspecified
+ *                       output (and may take long) but no access outside x_in,
+ *                       a_rows, y_perm or the workspace.
  *   x_in               the FFN's input rows, one of:
  *                        a_rows == NULL: x_perm [n_max,d], rows grouped by expert;
  *                        a_rows != NULL: the token matrix x [n_in,d]; row r of the
  *                          FFN input is x[a_rows[r]] (a_rows = row_token from
  *                          moe_permute), read in place without a permuted copy.
- *                          Requires n_in*d*sizeof(dtype) < 2^32 and 0 <= a_rows[r] < n_in.
+ *                          Requires n_in*d*sizeof(dtype) < 2^32; entries outside
+ *                          [0, n_in) are clamped into it on the device.
  *   n_in               rows of x_in when a_rows != NULL (ignored otherwise)
  *   a_rows   [n_max]   int32   NULL or the gather map described above
  *   offsets  [E+1]     int32   device array as written by moe_permute; empty experts allowed
@@ -132,8 +153,14 @@ moe_status moe_grouped_ffn(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_d
 
 /*
  * moe_combine: weighted un-permute.
+ * Passage: section 二 of "Domyn 团队在 Jupiter 超算完成 1 万亿参数 MoE 模型训练项目解析"
+ * (a token's output comes from the few experts it was routed to), mixed with the
+ * renormalised gate weights of moe_route.
  *   y_perm    [*,d]  dtype     expert outputs by row
- *   slot_row  [T,k]  int32     row of slot (t,j), negative = skipped
+ *   slot_row  [T,k]  int32     row of slot (t,j), negative = skipped; every
+ *                               non-negative row must exist in y_perm (the library
+ *                               does not know y_perm's row count: this is the
+ *                               caller's promise, kept by moe_permute's output)
  *   topk_w    [T,k]  float32   gate weights
  *   y         [T,d]  dtype     out: y[t] = sum_j topk_w[t,j] * y_perm[slot_row[t,j]]
  *                               (float32 sum); a token with no valid slot gets 0
@@ -144,6 +171,9 @@ moe_status moe_combine(int64_t T, int64_t d, int64_t k, moe_dtype dtype,
 
 /*
  * moe_layer_forward: the whole layer, route -> permute -> grouped FFN -> combine.
+ * Passages: those of the four calls above (the layer of the configuration table of
+ * "Training a 1T-Parameter MoE on EU public infrastructure with PyTorch and
+ * TorchTitan", routed as in section 二 of the Domyn page, dropless as in Pangu).
  *   x [T,d], w_router [E,d] | NULL, bias [E] | NULL, w_gate, w_up [E,F,d], w_down [E,d,F]
  *   y [T,d] out.
  *   When w_router is not NULL the router runs and topk_ids / topk_w, if not

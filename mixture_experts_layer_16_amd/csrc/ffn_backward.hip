@@ -47,13 +47,36 @@ constexpr int kWgradColumnGroup = 8;
 constexpr int kRowsRowChunk = 0;
 constexpr int kRowsColumnGroup = 0;
 
-// poff[e] = sum over e' < e of the row count of e' rounded up to 64 (one block).
-__global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __restrict__ offsets, int E,
-                                                           int32_t* __restrict__ poff) {
+// The caller's offsets made consistent, then padded:
+//   soff[e] = the running maximum of offsets[0..e] clamped to [0, n_max] (offsets
+//             that are non-decreasing and end at most at n_max pass through
+//             unchanged; any others still give disjoint segments inside the
+//             buffers), and every later kernel reads soff, never offsets;
+//   poff[e] = sum over e' < e of the row count of e' rounded up to 64 (one block).
+__global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __restrict__ offsets, int E, int64_t n_max,
+                                                           int32_t* __restrict__ soff, int32_t* __restrict__ poff) {
   __shared__ int wsum[16];
+  __shared__ int wmax[16];
+  __shared__ int bnd[kMaxExperts + 1];
   const int e = threadIdx.x;
-  const int v = e < E ? (offsets[e + 1] - offsets[e] + 63) / 64 * 64 : 0;
   const int lane = e & 63, wv = e >> 6;
+  int mx = e < E ? offsets[e] : INT32_MIN;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(mx, o, 64);
+    if (lane >= o) mx = max(mx, t);
+  }
+  if (lane == 63) wmax[wv] = mx;
+  __syncthreads();
+  int before = INT32_MIN;
+  for (int i = 0; i < wv; ++i) before = max(before, wmax[i]);
+  const int run = max(before, mx);                 // maximum of offsets[0..e]
+  if (e < E) bnd[e] = (int)clamp64(run, 0, n_max);
+  if (e == E - 1) bnd[E] = (int)clamp64(max(run, offsets[E]), 0, n_max);
+  __syncthreads();
+  if (e < E) soff[e] = bnd[e];
+  if (e == E - 1) soff[E] = bnd[E];
+  const int v = e < E ? (bnd[e + 1] - bnd[e] + 63) / 64 * 64 : 0;
   int incl = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -62,10 +85,10 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __rest
   }
   if (lane == 63) wsum[wv] = incl;
   __syncthreads();
-  int before = 0;
-  for (int i = 0; i < wv; ++i) before += wsum[i];
-  if (e < E) poff[e] = before + incl - v;
-  if (e == E - 1) poff[E] = before + incl;
+  int sum_before = 0;
+  for (int i = 0; i < wv; ++i) sum_before += wsum[i];
+  if (e < E) poff[e] = sum_before + incl - v;
+  if (e == E - 1) poff[E] = sum_before + incl;
 }
 
 // The transposed, padded activations are stored k-blocked: element (c, p) of an
@@ -76,12 +99,12 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __rest
 // 256 rows a megabyte apart (one address-translation page each).
 //
 // Element (c, p) for padded row p of expert e = source row offsets[e] + (p - poff[e])
-// (through rows[] when given), column col0 + c of the source (row stride ld_src);
-// zero past the expert's rows.  One 64 x 64 tile per block; blocks past poff[E] have
+// (through rows[] when given, its entries clamped to [0, n_src)), column col0 + c of
+// the source (row stride ld_src); zero past the expert's rows.  One 64 x 64 tile per block; blocks past poff[E] have
 // nothing to do; pblk_expert[p / 64] is the expert owning padded rows p .. p + 63.
 template <typename T, int KW>
 __global__ __launch_bounds__(256) void pad_transpose_kernel(const T* __restrict__ src, int64_t ld_src, int col0,
-                                                            const int32_t* __restrict__ rows,
+                                                            const int32_t* __restrict__ rows, int64_t n_src,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ poff,
                                                             const int32_t* __restrict__ pblk_expert, int E,
@@ -98,7 +121,7 @@ __global__ __launch_bounds__(256) void pad_transpose_kernel(const T* __restrict_
     T v = static_cast<T>(0.0f);
     if (r0 + j < n_e) {
       const int64_t sr = offsets[e] + r0 + j;
-      const int64_t row = rows ? (int64_t)rows[sr] : sr;
+      const int64_t row = rows ? (int64_t)clamp_row(rows[sr], n_src) : sr;
       v = src[row * ld_src + col0 + c0 + tx];
     }
     tile[j][tx] = v;
@@ -127,7 +150,7 @@ __global__ __launch_bounds__(256) void pad_block_experts_kernel(const int32_t* _
 // 16-bit elements: the same result as pad_transpose_kernel with KW = 64, in strips
 // of up to 8 tiles (grid.y walks the strips of the R source columns).
 __global__ __launch_bounds__(256) void pad_transpose16_kernel(const uint16_t* __restrict__ src, int64_t ld_src,
-                                                              int col0, const int32_t* __restrict__ rows,
+                                                              int col0, const int32_t* __restrict__ rows, int64_t n_src,
                                                               const int32_t* __restrict__ offsets,
                                                               const int32_t* __restrict__ poff,
                                                               const int32_t* __restrict__ pblk_expert, int E,
@@ -145,7 +168,7 @@ __global__ __launch_bounds__(256) void pad_transpose16_kernel(const uint16_t* __
       [&](int r) -> const uint16_t* {
         if (r0 + r >= n_e) return nullptr;
         const int64_t sr = offsets[e] + r0 + r;
-        const int64_t row = rows ? (int64_t)rows[sr] : sr;
+        const int64_t row = rows ? (int64_t)clamp_row(rows[sr], n_src) : sr;
         return src + row * ld_src + col0 + cs;
       },
       [&](int j, int c) { return blk + (int64_t)(cs + j * kTile + c) * kTile; });
@@ -194,8 +217,8 @@ void gemm(GemmArgs a, int num_cu, hipStream_t s) {
 }
 
 template <typename T, int BK>
-hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_in, const int32_t* a_rows,
-                          const int32_t* offsets, const void* w_gate, const void* w_up, const void* w_down,
+hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_in, int64_t n_in,
+                          const int32_t* a_rows, const int32_t* raw_offsets, const void* w_gate, const void* w_up, const void* w_down,
                           const void* dy_perm, void* dx_perm, float* dw_gate, float* dw_up, float* dw_down,
                           const FfnBackwardScratch& w, int num_cu, hipStream_t s) {
   const int64_t np = w.n_pad;   // columns of the padded transposed layouts
@@ -203,8 +226,9 @@ hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const 
   const T* Wu = static_cast<const T*>(w_up);
   const T* Wd = static_cast<const T*>(w_down);
 
-  // padded expert column ranges; transposed weights
-  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(1024), 0, s, offsets, (int)E, w.poff);
+  // consistent and padded expert row ranges; transposed weights
+  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(1024), 0, s, raw_offsets, (int)E, n_max, w.soff, w.poff);
+  const int32_t* offsets = w.soff;
   // (whole, regular matrices: one tile per block keeps the most tiles in flight)
   auto transpose_into = [&](const T* src, int rows, int cols, T* dst, int64_t ld_dst, int coff, int64_t batch) {
     hipLaunchKernelGGL((transpose_into_kernel<T>), dim3((unsigned)(cols / kTile), (unsigned)(rows / kTile), (unsigned)E),
@@ -230,6 +254,7 @@ hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const 
   }
   // recompute G, U; dG | dU and H
   GemmArgs a2 = args_grouped(x_in, a_rows, w_gate, w_up, F * d, offsets, (int)E, n_max, (int)F, (int)d, w.dgu);
+  a2.a_rows_n = n_in;
   a2.D = w.dh;
   a2.C2 = w.h;
   a2.ldc = 2 * F;
@@ -252,12 +277,12 @@ hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const 
   auto pad_transpose = [&](const void* src, int64_t ld_src, int col0, const int32_t* rows, void* dst, int64_t R) {
     if constexpr (sizeof(T) == 2 && BK == kTile) {
       hipLaunchKernelGGL(pad_transpose16_kernel, dim3(nblk, (unsigned)((R / kTile + 7) / 8)), dim3(256), 0, s,
-                         static_cast<const uint16_t*>(src), ld_src, col0, rows, offsets, w.poff, w.pblk_expert,
-                         (int)E, static_cast<uint16_t*>(dst), R);
+                         static_cast<const uint16_t*>(src), ld_src, col0, rows, n_in, offsets, w.poff,
+                         w.pblk_expert, (int)E, static_cast<uint16_t*>(dst), R);
     } else {
       hipLaunchKernelGGL((pad_transpose_kernel<T, BK>), dim3(nblk, (unsigned)(R / kTile)), dim3(256), 0, s,
-                         static_cast<const T*>(src), ld_src, col0, rows, offsets, w.poff, w.pblk_expert, (int)E,
-                         static_cast<T*>(dst), R);
+                         static_cast<const T*>(src), ld_src, col0, rows, n_in, offsets, w.poff, w.pblk_expert,
+                         (int)E, static_cast<T*>(dst), R);
     }
   };
   pad_transpose(x_in, d, 0, a_rows, w.x_t, d);
@@ -287,15 +312,15 @@ hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const 
 }  // namespace
 
 hipError_t launch_grouped_ffn_backward(int dtype, int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_in,
-                                       const int32_t* a_rows, const int32_t* offsets, const void* w_gate,
-                                       const void* w_up, const void* w_down, const void* dy_perm, void* dx_perm,
-                                       float* dw_gate, float* dw_up, float* dw_down, const FfnBackwardScratch& w,
-                                       int num_cu, hipStream_t s) {
+                                       int64_t n_in, const int32_t* a_rows, const int32_t* offsets,
+                                       const void* w_gate, const void* w_up, const void* w_down, const void* dy_perm,
+                                       void* dx_perm, float* dw_gate, float* dw_up, float* dw_down,
+                                       const FfnBackwardScratch& w, int num_cu, hipStream_t s) {
   if (dtype == 1)
-    return ffn_backward_t<bf16, 64>(n_max, d, E, F, x_in, a_rows, offsets, w_gate, w_up, w_down, dy_perm, dx_perm,
-                                    dw_gate, dw_up, dw_down, w, num_cu, s);
-  return ffn_backward_t<float, 32>(n_max, d, E, F, x_in, a_rows, offsets, w_gate, w_up, w_down, dy_perm, dx_perm,
-                                   dw_gate, dw_up, dw_down, w, num_cu, s);
+    return ffn_backward_t<bf16, 64>(n_max, d, E, F, x_in, n_in, a_rows, offsets, w_gate, w_up, w_down, dy_perm,
+                                    dx_perm, dw_gate, dw_up, dw_down, w, num_cu, s);
+  return ffn_backward_t<float, 32>(n_max, d, E, F, x_in, n_in, a_rows, offsets, w_gate, w_up, w_down, dy_perm,
+                                   dx_perm, dw_gate, dw_up, dw_down, w, num_cu, s);
 }
 
 }  // namespace moe

@@ -24,6 +24,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "tile_walk.h"
 
 namespace moe {
 
@@ -62,6 +63,8 @@ struct GemmArgs {
   const void* A;          // [rows, K]; group g owns rows seg[g] .. seg[g+1]-1
   const int32_t* a_rows;  // nullptr, or a gather map: logical row r is row a_rows[r] of A
                           // (A's byte size must then stay below 4 GiB)
+  int64_t a_rows_n;       // a_rows != nullptr: rows of A; map entries are clamped to
+                          // [0, a_rows_n) (they come from device memory)
   const void* B0;         // group g: B0 + g * b_stride elements, [N, K]
   const void* B1;         // EPI_SWIGLU: the "up" matrix, same layout as B0
   int64_t b_stride;       // elements between two groups' B matrices
@@ -271,32 +274,59 @@ struct GemmTile {
   }
 };
 
-// Exclusive prefix over groups of the number of tiles each owns, into tstart[0..G].
+// With offsets (seg != nullptr): the segment bounds of tile_walk.h into
+// gbound[0..G] (the running maximum of seg clamped to [0, M]).  Then the exclusive
+// prefix over groups of the tiles each owns into tstart[0..G], saturated at
+// INT32_MAX.  One wavefront does the work; the barriers publish it.
 template <int BM, int NTHREADS>
-__device__ void build_tile_prefix(const int32_t* seg, int G, int64_t M, int64_t group_rows, int ntn, int* tstart) {
+__device__ void build_tile_prefix(const int32_t* seg, int G, int64_t M, int64_t group_rows, int ntn, int* tstart,
+                                  int* gbound) {
   const int tid = threadIdx.x;
+  if (seg) {
+    if (tid < 64) {
+      const int lane = tid;
+      const int nb = G + 1;                         // bounds 0 .. G
+      const int per = (nb + 63) / 64;
+      const int lo = min(nb, lane * per), hi = min(nb, lo + per);
+      int64_t m = INT64_MIN;
+      for (int i = lo; i < hi; ++i) m = max(m, (int64_t)seg[i]);
+      int64_t incl = m;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int64_t v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl = max(incl, v);
+      }
+      int64_t run = __shfl_up(incl, 1, 64);         // maximum of the raw offsets before lo
+      if (lane == 0) run = INT64_MIN;
+      for (int i = lo; i < hi; ++i) {
+        const int64_t raw = seg[i];
+        gbound[i] = (int)segment_bound(run, raw, M);
+        run = max(run, raw);
+      }
+    }
+    __syncthreads();
+  }
   if (tid < 64) {
     const int lane = tid;
     const int per = (G + 63) / 64;
     const int lo = min(G, lane * per), hi = min(G, lo + per);
-    int sum = 0;
-    for (int g = lo; g < hi; ++g) {
-      const int64_t rows = seg ? (int64_t)seg[g + 1] - seg[g] : (group_rows > 0 ? group_rows : M);
-      sum += (int)((rows + BM - 1) / BM) * ntn;
-    }
-    int incl = sum;
+    auto rows_of = [&](int g) -> int64_t {
+      return seg ? (int64_t)gbound[g + 1] - gbound[g] : (group_rows > 0 ? group_rows : M);
+    };
+    int64_t sum = 0;
+    for (int g = lo; g < hi; ++g) sum += group_tiles(rows_of(g), BM, ntn);
+    int64_t incl = sum;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
+      const int64_t v = __shfl_up(incl, o, 64);
       if (lane >= o) incl += v;
     }
-    int run = incl - sum;
+    int64_t run = incl - sum;
     for (int g = lo; g < hi; ++g) {
-      tstart[g] = run;
-      const int64_t rows = seg ? (int64_t)seg[g + 1] - seg[g] : (group_rows > 0 ? group_rows : M);
-      run += (int)((rows + BM - 1) / BM) * ntn;
+      tstart[g] = saturate_tiles(run);
+      run += group_tiles(rows_of(g), BM, ntn);
     }
-    if (lane == 63) tstart[G] = incl;
+    if (lane == 63) tstart[G] = saturate_tiles(incl);
   }
   __syncthreads();
 }
@@ -337,6 +367,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   constexpr int kEpiWaveBytes = 32 * kEpiRowBytes;  // one wave's staging buffer: 32 rows
   __shared__ __attribute__((aligned(1024))) char smem[Cfg::kLdsBytes];
   __shared__ int tstart[kMaxGroups + 1];
+  __shared__ int gbound[kMaxGroups + 1];   // segment bounds (with offsets)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -348,7 +379,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   // equal groups (a batch of matrices): group g owns tiles [g * per_g, (g+1) * per_g)
   const bool uniform = GRP && p.seg == nullptr;
   const int per_g = uniform ? (int)((p.group_rows > 0 ? p.group_rows : p.M) + BM - 1) / BM * ntn : 0;
-  if (!uniform) build_tile_prefix<BM, NT>(p.seg, G, p.M, GRP ? p.group_rows : 0, ntn, tstart);
+  if (!uniform) build_tile_prefix<BM, NT>(p.seg, G, p.M, GRP ? p.group_rows : 0, ntn, tstart, gbound);
   const int total = uniform ? G * per_g : __builtin_amdgcn_readfirstlane(tstart[G]);
   const int K = p.K;
   const int64_t lda = (STR && p.lda) ? p.lda : K, ldb = (STR && p.ldb) ? p.ldb : K;
@@ -373,36 +404,21 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
       t.g = tile / per_g;
       local = tile - t.g * per_g;
     } else {
-      int lo = 0, hi = G;                    // largest g with tstart[g] <= tile
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (tstart[mid] <= tile) lo = mid; else hi = mid;
-      }
-      t.g = __builtin_amdgcn_readfirstlane(lo);
+      t.g = __builtin_amdgcn_readfirstlane(find_group(tstart, G, tile));
       local = tile - __builtin_amdgcn_readfirstlane(tstart[t.g]);
     }
     const int64_t grows = GRP ? p.group_rows : 0;
-    // offsets are read-only here: read them through the scalar cache
-    const int32_t __attribute__((address_space(4)))* sseg =
-        (const int32_t __attribute__((address_space(4)))*)p.seg;
-    const int64_t seg_lo = p.seg ? (int64_t)sseg[t.g] : (int64_t)t.g * grows;
-    const int64_t seg_hi = p.seg ? (int64_t)sseg[t.g + 1] : (grows > 0 ? seg_lo + grows : p.M);
-    // Within a group the tiles run in chunks of SM row tiles; inside a chunk, in
-    // column groups of NG column tiles; inside a column group, row tile by row
-    // tile.  Consecutive tiles then share A rows (same row tile) and B columns
+    // offsets: the clamped segment bounds built with the tile prefix
+    const int64_t seg_lo = p.seg ? (int64_t)gbound[t.g] : (int64_t)t.g * grows;
+    const int64_t seg_hi = p.seg ? (int64_t)gbound[t.g + 1] : (grows > 0 ? seg_lo + grows : p.M);
+    // Within a group the tiles run in chunks of m_chunk row tiles; inside a chunk,
+    // in column groups of n_group column tiles; inside a column group, row tile by
+    // row tile.  Consecutive tiles then share A rows (same row tile) and B columns
     // (same column group), and a chunk's A rows stay hot while its column groups
     // go by.
     const int mtc = (int)((seg_hi - seg_lo + BM - 1) / BM);
-    const int SM = (p.m_chunk > 0 && p.m_chunk < mtc) ? p.m_chunk : mtc;
-    const int NG = (p.n_group > 0 && p.n_group < ntn) ? p.n_group : ntn;
-    const int ch = local / (SM * ntn);
-    const int base_m = ch * SM;
-    const int sm = min(SM, mtc - base_m);
-    const int l = local - ch * SM * ntn;
-    const int cg = l / (sm * NG);
-    const int l2 = l - cg * sm * NG;
-    const int sz = min(NG, ntn - cg * NG);
-    const int mt = base_m + l2 / sz, nt = cg * NG + l2 % sz;
+    const TileSpot spot = tile_spot(local, mtc, ntn, p.m_chunk, p.n_group);
+    const int mt = spot.mt, nt = spot.nt;
     t.m0 = seg_lo + (int64_t)mt * BM;
     t.mrel = (int64_t)mt * BM;
     t.n0 = nt * NOUT;
@@ -421,7 +437,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     for (int i = 0; i < CPA; ++i) {
       const int row = (i * NT + tid) * 16 / RB;
       const int r = min(row, t.rows_valid - 1);              // rows past the segment: any valid row
-      arow[i] = p.a_rows ? p.a_rows[t.m0 + r] : r;
+      arow[i] = p.a_rows ? clamp_row(p.a_rows[t.m0 + r], p.a_rows_n) : r;
     }
   };
 

@@ -36,13 +36,14 @@ constexpr int kDownColumnGroup = 2;
 // Tile configuration: 256 x 256 output tiles, BK-deep k-slices, STAGES-deep LDS
 // ring, WM x WN wavefronts, MFMA operands read PD 16-k sub-steps ahead.
 template <typename T, int BK, int STAGES, int WM, int WN, int PD>
-void run(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm, const int32_t* a_rows,
+void run(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm, int64_t n_in, const int32_t* a_rows,
          const int32_t* offsets,
          const void* w_gate, const void* w_up, const void* w_down, void* y_perm, void* h, int num_cu,
          hipStream_t stream) {
   GemmArgs gu{};
   gu.A = x_perm;
   gu.a_rows = a_rows;
+  gu.a_rows_n = n_in;
   gu.B0 = w_gate;
   gu.B1 = w_up;
   gu.b_stride = F * d;
@@ -82,12 +83,15 @@ void run(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm, con
 }  // namespace
 
 hipError_t launch_grouped_ffn(int dtype, int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm,
-                              const int32_t* a_rows, const int32_t* offsets, const void* w_gate, const void* w_up, const void* w_down,
-                              void* y_perm, void* h, int num_cu, hipStream_t stream) {
+                              int64_t n_in, const int32_t* a_rows, const int32_t* offsets, const void* w_gate,
+                              const void* w_up, const void* w_down, void* y_perm, void* h, int num_cu,
+                              hipStream_t stream) {
   if (dtype == 1)
-    run<bf16, 64, 2, 4, 2, 1>(n_max, d, E, F, x_perm, a_rows, offsets, w_gate, w_up, w_down, y_perm, h, num_cu, stream);
+    run<bf16, 64, 2, 4, 2, 1>(n_max, d, E, F, x_perm, n_in, a_rows, offsets, w_gate, w_up, w_down, y_perm, h, num_cu,
+                              stream);
   else
-    run<float, 32, 2, 4, 2, 1>(n_max, d, E, F, x_perm, a_rows, offsets, w_gate, w_up, w_down, y_perm, h, num_cu, stream);
+    run<float, 32, 2, 4, 2, 1>(n_max, d, E, F, x_perm, n_in, a_rows, offsets, w_gate, w_up, w_down, y_perm, h,
+                               num_cu, stream);
   return hipGetLastError();
 }
 

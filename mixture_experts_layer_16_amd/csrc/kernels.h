@@ -26,9 +26,12 @@ hipError_t launch_permute(int dtype, int64_t T, int64_t d, int64_t E, int64_t k,
 constexpr int kPermuteBlockTokens = 256;
 
 // Grouped SwiGLU FFN: h = silu(X W_g^T) * (X W_u^T); y_perm = h W_d^T, where row r
-// of X is x_perm[r], or x[a_rows[r]] when a gather map is given.
+// of X is x_perm[r], or x[a_rows[r]] when a gather map is given (x has n_in rows;
+// map entries are clamped to them).  The offsets are clamped into consistent
+// segments inside [0, n_max) on the device.
 hipError_t launch_grouped_ffn(int dtype, int64_t n_max, int64_t d, int64_t E, int64_t F,
-                              const void* x_perm, const int32_t* a_rows, const int32_t* offsets, const void* w_gate,
+                              const void* x_perm, int64_t n_in, const int32_t* a_rows, const int32_t* offsets,
+                              const void* w_gate,
                               const void* w_up, const void* w_down, void* y_perm, void* h,
                               int num_cu, hipStream_t stream);
 
@@ -43,6 +46,7 @@ hipError_t launch_newton_schulz(int64_t n, int64_t R, int64_t C, int64_t steps, 
 // Backward of the grouped SwiGLU FFN: dx_perm and the float32 weight gradients
 // from dy_perm.  Scratch (caller-carved; "I/O" = the dtype's element type):
 struct FfnBackwardScratch {
+  int32_t* soff;   // [E+1] the caller's offsets clamped into consistent segments
   int32_t* poff;   // [E+1] padded expert column offsets
   int32_t* pblk_expert;  // [n_pad / 64] expert of each 64-wide padded column block
   void* wd_t;      // [E, F, d]   W_d transposed (float32 layers only)
@@ -59,7 +63,7 @@ struct FfnBackwardScratch {
   int64_t n_pad;   // >= sum over experts of rows rounded up to 64; a multiple of 64
 };
 hipError_t launch_grouped_ffn_backward(int dtype, int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_in,
-                                       const int32_t* a_rows, const int32_t* offsets, const void* w_gate,
+                                       int64_t n_in, const int32_t* a_rows, const int32_t* offsets, const void* w_gate,
                                        const void* w_up, const void* w_down, const void* dy_perm, void* dx_perm,
                                        float* dw_gate, float* dw_up, float* dw_down, const FfnBackwardScratch& w,
                                        int num_cu, hipStream_t stream);

@@ -111,6 +111,7 @@ struct Carver {
 void carve_ffn_backward(Carver& c, moe::FfnBackwardScratch& w, int64_t n_max, int64_t d, int64_t E, int64_t F,
                         size_t es) {
   const int64_t n_pad = (n_max + 63 * E + 63) / 64 * 64;
+  w.soff = static_cast<int32_t*>(c.take((size_t)(E + 1) * 4));
   w.poff = static_cast<int32_t*>(c.take((size_t)(E + 1) * 4));
   w.pblk_expert = static_cast<int32_t*>(c.take((size_t)(n_pad / 64) * 4));
   // transposed weight copies: float32 only (16-bit weights are read in place)
@@ -211,8 +212,8 @@ moe_status moe_grouped_ffn(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_d
   if (workspace_step(ws, ws_bytes, need, &st)) return st;
   int ncu = 0;
   if ((st = num_cu(&ncu)) != MOE_OK) return st;
-  return hip_status(moe::launch_grouped_ffn(dtype, n_max, d, E, F, x_in, a_rows, offsets, w_gate, w_up, w_down,
-                                            y_perm, ws, ncu, static_cast<hipStream_t>(stream)));
+  return hip_status(moe::launch_grouped_ffn(dtype, n_max, d, E, F, x_in, a_rows ? n_in : n_max, a_rows, offsets,
+                                            w_gate, w_up, w_down, y_perm, ws, ncu, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_dtype dtype,
@@ -245,9 +246,9 @@ moe_status moe_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int64_t
   if ((st = num_cu(&ncu)) != MOE_OK) return st;
   Carver cv(ws);
   carve_ffn_backward(cv, w, n_max, d, E, F, es);
-  return hip_status(moe::launch_grouped_ffn_backward(dtype, n_max, d, E, F, x_in, a_rows, offsets, w_gate, w_up,
-                                                     w_down, dy_perm, dx_perm, dw_gate, dw_up, dw_down, w, ncu,
-                                                     static_cast<hipStream_t>(stream)));
+  return hip_status(moe::launch_grouped_ffn_backward(dtype, n_max, d, E, F, x_in, a_rows ? n_in : n_max, a_rows,
+                                                     offsets, w_gate, w_up, w_down, dy_perm, dx_perm, dw_gate, dw_up,
+                                                     dw_down, w, ncu, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_combine_backward(int64_t T, int64_t d, int64_t k, moe_dtype dtype, const void* dy,
@@ -360,7 +361,7 @@ moe_status moe_layer_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_
       MOE_OK)
     return st;
   if ((st = hip_status(moe::launch_grouped_ffn_backward(dtype, slots, d, E, F, in_place ? x : x_perm,
-                                                        in_place ? row_token : nullptr, offsets, w_gate, w_up,
+                                                        in_place ? T : slots, in_place ? row_token : nullptr, offsets, w_gate, w_up,
                                                         w_down, dy_perm, dx_perm, dw_gate, dw_up, dw_down, fw, ncu,
                                                         s))) != MOE_OK)
     return st;
@@ -471,7 +472,7 @@ moe_status moe_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
                                            in_place ? nullptr : y_perm, counts, s))) != MOE_OK)
     return st;
   if ((st = hip_status(moe::launch_grouped_ffn(dtype, (int64_t)slots, d, E, F, in_place ? x : y_perm,
-                                               in_place ? row_token : nullptr, offsets, w_gate, w_up, w_down,
+                                               in_place ? T : (int64_t)slots, in_place ? row_token : nullptr, offsets, w_gate, w_up, w_down,
                                                y_perm, h, ncu, s))) != MOE_OK)
     return st;
   return hip_status(moe::launch_combine(dtype, T, d, k, y_perm, slot_row, w, y, s));

@@ -13,8 +13,12 @@
 //               row = offsets[e] + block_prefix[b][e] + rank;
 //               then (unless only indices are wanted) the block copies each
 //               token's row to its k destinations with 16-byte vectors.
-// No global atomics: two runs give identical bits.  A token's ids must be
-// distinct; a negative id (or one >= E) marks a slot that is skipped.
+// No global atomics: two runs give identical bits.  A negative id (or one >= E)
+// marks a slot that is skipped.  A token that names the same expert in two slots
+// (top-k never does; pre-routed input might) gets two rows, in slot order, like
+// any counting sort of the slots: the bitmap cannot count such a token twice, so
+// an expert with a repeated (token, expert) pair in a block is ranked by a serial
+// walk over the block's slots instead.
 #include "common.h"
 #include "kernels.h"
 
@@ -89,9 +93,15 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const T* __restric
                                                               int32_t* __restrict__ slot_row, T* __restrict__ x_perm) {
   __shared__ uint32_t bits[kMaxExperts * WPB];
   __shared__ int base[kMaxExperts];
+  __shared__ uint8_t repeated[kMaxExperts];   // expert e has a token naming it twice in this block
+  __shared__ int any_repeated;
   const int b = blockIdx.x;
   for (int i = threadIdx.x; i < E * WPB; i += 256) bits[i] = 0u;
-  for (int e = threadIdx.x; e < E; e += 256) base[e] = offsets[e] + block_prefix[(int64_t)b * E + e];
+  for (int e = threadIdx.x; e < E; e += 256) {
+    base[e] = offsets[e] + block_prefix[(int64_t)b * E + e];
+    repeated[e] = 0;
+  }
+  if (threadIdx.x == 0) any_repeated = 0;
   __syncthreads();
   const int t0 = b * TB;
   const int64_t s0 = (int64_t)t0 * k;
@@ -100,30 +110,49 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const T* __restric
     const int e = ids[s];
     if (e >= 0 && e < E) {
       const int tl = (int)(s / k) - t0;
-      atomicOr(&bits[e * WPB + (tl >> 5)], 1u << (tl & 31));
+      const uint32_t m = 1u << (tl & 31);
+      if (atomicOr(&bits[e * WPB + (tl >> 5)], m) & m) {
+        repeated[e] = 1;
+        any_repeated = 1;
+      }
     }
   }
   __syncthreads();
 
-  // indices: one thread per slot
+  // indices: one thread per slot (experts with a repeated pair: below)
   for (int64_t s = s0 + threadIdx.x; s < s1; s += 256) {
     const int e = ids[s];
     const int t = (int)(s / k);
-    int row = -1;
     if (e >= 0 && e < E) {
+      if (repeated[e]) continue;
       const int tl = t - t0;
       const uint32_t* w = bits + e * WPB;
       int rank = __popc(w[tl >> 5] & ((1u << (tl & 31)) - 1u));
       for (int q = 0; q < (tl >> 5); ++q) rank += __popc(w[q]);
-      row = base[e] + rank;
+      const int row = base[e] + rank;
       row_token[row] = t;
+      slot_row[s] = row;
+    } else {
+      slot_row[s] = -1;
     }
-    slot_row[s] = row;
+  }
+  if (any_repeated) {
+    // one thread per such expert walks the block's slots in (token, slot) order
+    for (int e = threadIdx.x; e < E; e += 256) {
+      if (!repeated[e]) continue;
+      int row = base[e];
+      for (int64_t s = s0; s < s1; ++s)
+        if (ids[s] == e) {
+          row_token[row] = (int)(s / k);
+          slot_row[s] = row++;
+        }
+    }
   }
   if (x_perm == nullptr) return;
+  __syncthreads();   // this block's slot_row entries are written
 
   // rows: each wavefront copies its tokens' rows to their destinations with
-  // 16-byte vectors (destination rows recomputed from the bitmap)
+  // 16-byte vectors
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nt = min(TB, Tn - t0);
   constexpr int EPC = 16 / sizeof(T);
@@ -131,12 +160,8 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const T* __restric
   for (int tl = wave; tl < nt; tl += 4) {
     const int t = t0 + tl;
     for (int j = 0; j < k; ++j) {
-      const int e = ids[(int64_t)t * k + j];
-      if (e < 0 || e >= E) continue;
-      const uint32_t* w = bits + e * WPB;
-      int rank = __popc(w[tl >> 5] & ((1u << (tl & 31)) - 1u));
-      for (int q = 0; q < (tl >> 5); ++q) rank += __popc(w[q]);
-      const int row = base[e] + rank;
+      const int row = slot_row[(int64_t)t * k + j];
+      if (row < 0) continue;
       const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)t * d);
       u32x4* dst = reinterpret_cast<u32x4*>(x_perm + (int64_t)row * d);
       for (int c = lane; c < nchunk; c += 64) dst[c] = src[c];

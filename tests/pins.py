@@ -295,4 +295,10 @@ def pin_page_parameter_identity(orc):
     assert active_routed <= g["active_params_billion_per_token"]
 
 
+def pin_to_f64_reads_bf16_bits(orc):
+    """uint16 inputs are bf16 bit patterns: all 65,536 against torch's conversion."""
+    from pin_bits import check_bf16_bits
+    check_bf16_bits(orc.to_f64)
+
+
 PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

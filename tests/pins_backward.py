@@ -97,4 +97,10 @@ def pin_grouped_backward_is_per_expert(orc):
         np.testing.assert_allclose(dwd[e], t[3].grad.numpy(), rtol=0, atol=1e-12)
 
 
+def pin_to_f64_reads_bf16_bits(orc):
+    """uint16 inputs are bf16 bit patterns: all 65,536 against torch's conversion."""
+    from pin_bits import check_bf16_bits
+    check_bf16_bits(orc.to_f64)
+
+
 PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

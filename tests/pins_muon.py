@@ -124,4 +124,10 @@ def pin_ns_batch_is_per_matrix(orc):
         np.testing.assert_array_equal(got[i], orc.newton_schulz(G[i]))
 
 
+def pin_to_f64_reads_bf16_bits(orc):
+    """uint16 inputs are bf16 bit patterns: all 65,536 against torch's conversion."""
+    from pin_bits import check_bf16_bits
+    check_bf16_bits(orc.to_f64)
+
+
 PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -225,7 +225,8 @@ def bwd_ws(n_max, d, E, F, es=2):
     n_pad = (n_max + 63 * E + 63) // 64 * 64
     # transposed weight copies only for float32 layers (16-bit weights are read in place)
     wcopies = ru(E * F * d * es) + ru(E * d * 2 * F * es) if es == 4 else 0
-    return (ru((E + 1) * 4) + ru(n_pad // 64 * 4) + wcopies + ru(n_max * F * 4)
+    # sanitised offsets, padded offsets, block owners
+    return (2 * ru((E + 1) * 4) + ru(n_pad // 64 * 4) + wcopies + ru(n_max * F * 4)
             + ru(n_max * 2 * F * es) + ru(n_max * F * es) + 2 * ru(d * n_pad * es) + 3 * ru(F * n_pad * es))
 
 

@@ -3,8 +3,11 @@ configuration that bench.py times (moe_layer_forward).  The oracle checks:
   * routing of EVERY token: ids bit-exact and gate weights within 1e-6 when the
     oracle selects on the GPU's logits; the logits themselves on a token sample;
   * the expert offsets, bit-exact;
-  * the grouped FFN on sampled rows of sampled experts (stage entry points);
-  * the layer output on sampled tokens;
+  * the grouped FFN (stage entry points) on EVERY row of the largest expert's
+    first two chunks of 16 row tiles and of its last chunk (the tile order walks
+    a large expert chunk by chunk), and on sampled rows of the smallest non-empty
+    expert and two random ones;
+  * the layer output on 256 sampled tokens (plus a token with no local slot);
   * the layer entry point equals the stage-by-stage path bit for bit.
 """
 import numpy as np
@@ -21,16 +24,12 @@ DEV = "cuda:0"
 FULL = ["page_balanced", "page_seq64k_skewed", "ep_rank_share"]
 
 
-class ExpertCache:
-    """float64 host copies of whole experts, fetched once each."""
+def expert_f64(inp, e):
+    """Exact float64 host copies of expert e's three matrices (widened on the device)."""
+    return tuple(inp[n][e].to(torch.float64).cpu().numpy() for n in ("w_gate", "w_up", "w_down"))
 
-    def __init__(self, inp):
-        self.inp, self.c = inp, {}
 
-    def __call__(self, e):
-        if e not in self.c:
-            self.c[e] = tuple(f64(self.inp[n][e]) for n in ("w_gate", "w_up", "w_down"))
-        return self.c[e]
+ROW_CHUNK = 16 * 256   # rows of one chunk of the forward GEMMs' tile order
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -64,24 +63,22 @@ def test_full_size_sampled_parity(name):
     print(f"[full-size] {name}: expert rows min {counts.min()} max {counts.max()} empty {(counts == 0).sum()}",
           flush=True)
 
-    experts = ExpertCache(inp)
-
-    # layer output on sampled tokens (tokens with no local slot included when present)
+    # layer output on 256 sampled tokens (a token with no local slot included when
+    # present), the reference one expert at a time
     has = (ref_ids >= 0).any(1)
-    St = list(rng.choice(np.nonzero(has)[0], 6, replace=False))
+    St = list(rng.choice(np.nonzero(has)[0], 256, replace=False))
     if (~has).any():
         St.append(int(np.nonzero(~has)[0][0]))
-    xs = f64(inp["x"][St])
-    y_ref = np.zeros((len(St), wl.d))
-    for i, t in enumerate(St):
-        for j in range(wl.k):
-            e = int(ref_ids[t, j])
-            if e >= 0:
-                y_ref[i] += ref_w[t, j] * orc.expert_ffn(xs[i:i + 1], *experts(e))[0]
-    assert_close(f64(L.y[St]), y_ref, wl.dtype, "y (sampled tokens)")
+    St = np.array(St)
+    xs = f64(inp["x"][torch.from_numpy(St).to(DEV)])
+    y_ref = np.zeros((St.size, wl.d))
+    for e in np.unique(ref_ids[St][ref_ids[St] >= 0]):
+        pos, slot = np.nonzero(ref_ids[St] == e)
+        ye = orc.expert_ffn(xs[pos], *expert_f64(inp, int(e)))
+        y_ref[pos] += ref_w[St[pos], slot][:, None] * ye
+    assert_close(f64(L.y[torch.from_numpy(St).to(DEV)]), y_ref, wl.dtype, "y (256 sampled tokens)")
 
-    # the stage entry points: bit-equal to the layer entry point, and the grouped
-    # FFN on sampled rows of the largest, the smallest non-empty and two random experts
+    # the stage entry points: bit-equal to the layer entry point
     if routed:
         ids, w, _ = B.moe_route(inp["x"], inp["w_router"], wl.k, bias=inp["bias"], want_logits=False)
     else:
@@ -91,10 +88,24 @@ def test_full_size_sampled_parity(name):
     y = B.moe_combine(yp, sr, w)
     torch.cuda.synchronize()
     assert bits_equal(y, L.y)
+
+    def check_rows(e, rows, what):
+        idx = torch.from_numpy(rows.astype(np.int64)).to(DEV)
+        X = inp["x"][torch.from_numpy(r_rt[rows].astype(np.int64)).to(DEV)].to(torch.float64).cpu().numpy()
+        ref = orc.expert_ffn(X, *expert_f64(inp, e))
+        assert_close(f64(yp[idx]), ref, wl.dtype, what)
+
+    # every row of the largest expert's first two chunks and of its last chunk
+    big = int(np.argmax(counts))
+    lo, hi = int(r_off[big]), int(r_off[big + 1])
+    last = lo + (hi - lo - 1) // ROW_CHUNK * ROW_CHUNK
+    rows = np.unique(np.concatenate([np.arange(lo, min(hi, lo + 2 * ROW_CHUNK)), np.arange(last, hi)]))
+    print(f"[full-size] {name}: expert {big} ({hi - lo} rows): {rows.size} rows compared", flush=True)
+    check_rows(big, rows, f"y_perm rows of expert {big}")
+    # sampled rows of the smallest non-empty expert and two random ones
     nz = np.nonzero(counts)[0]
-    pick = {int(np.argmax(counts)), int(nz[np.argmin(counts[nz])])} | set(rng.choice(nz, 2, replace=False).tolist())
-    for e in sorted(pick):
+    pick = {int(nz[np.argmin(counts[nz])])} | set(rng.choice(nz, 2, replace=False).tolist())
+    for e in sorted(pick - {big}):
         lo, hi = int(r_off[e]), int(r_off[e + 1])
         rows = np.unique(np.concatenate([[lo, hi - 1], rng.integers(lo, hi, 14)]))
-        ref = orc.expert_ffn(f64(inp["x"][torch.from_numpy(r_rt[rows].astype(np.int64)).to(DEV)]), *experts(e))
-        assert_close(f64(yp[torch.from_numpy(rows).to(DEV)]), ref, wl.dtype, f"y_perm rows of expert {e}")
+        check_rows(e, rows, f"y_perm rows of expert {e}")

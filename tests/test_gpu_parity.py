@@ -114,6 +114,13 @@ def test_permute_bit_exact(T, E, k, drop, dtype):
     ([1, 2, 300, 0, 64], 128, 64, torch.float32),
     ([1000], 512, 256, torch.bfloat16),
     ([0, 0, 7], 64, 64, torch.bfloat16),
+    # an expert past one chunk of 16 row tiles of the tile order (4,400 rows = 18 row
+    # tiles: a full chunk and a short one), odd column-tile counts in both GEMMs
+    # (gate/up 384 / 128 = 3, down 768 / 256 = 3)
+    ([4400, 0, 300, 37], 768, 384, torch.bfloat16),
+    # 20 row tiles, gate/up 192 / 128: one full and one half column tile, down one tile
+    ([5000, 0, 3], 64, 192, torch.bfloat16),
+    ([4200, 5], 128, 64, torch.float32),
 ])
 def test_grouped_ffn_matches_oracle(counts, d, F, dtype):
     E = len(counts)
@@ -288,3 +295,81 @@ def test_identity_router_crafts_exact_ties(E, k, T):
     inp["w_router"] = torch.eye(E, device=DEV, dtype=torch.bfloat16)
     L, _ = _layer_vs_oracle(inp, wl)
     assert np.array_equal(L.logits.cpu().numpy() + 0.0, vals + 0.0)
+
+
+# ---------------------------------------------------------------------------
+# an expert larger than one chunk of the tile order, through the whole layer
+# ---------------------------------------------------------------------------
+
+def test_layer_with_an_expert_past_one_row_tile_chunk():
+    # Zipf routing bias over 5 experts, top-2 of 12,000 tokens: the favoured expert
+    # gets well over 16 row tiles (4,096 rows), so the grouped GEMMs walk its tiles
+    # in several chunks, the last one short; every output element is compared
+    wl = W.Workload("long_expert", T=12000, d=256, E=5, k=2, F=384, dtype=torch.bfloat16, routing="router_bias")
+    inp = _inputs(wl)
+    L = _run_layer(inp, wl)
+    gl = L.logits.cpu().numpy().astype(np.float64)
+    counts = np.diff(i64(L.offsets))
+    print(f"[long expert] rows per expert {counts.tolist()}", flush=True)
+    assert counts.max() > 16 * 256 and counts.max() % (16 * 256) != 0
+    ref = orc.layer_forward(f64(inp["x"]), f64(inp["w_router"]), f64(inp["bias"]), LazyExperts(inp["w_gate"]),
+                            LazyExperts(inp["w_up"]), LazyExperts(inp["w_down"]), wl.k, selection_logits=gl)
+    assert np.array_equal(i64(L.topk_ids), ref["ids"])
+    assert np.array_equal(i64(L.offsets), ref["offsets"])
+    assert_close(f64(L.y), ref["y"], wl.dtype, "y")
+    # y_perm of the stage path, every row
+    off, rt, sr, _ = B.moe_permute(inp["x"], L.topk_ids, wl.E, copy_rows=False)
+    yp = B.moe_grouped_ffn(inp["x"], off, inp["w_gate"], inp["w_up"], inp["w_down"], a_rows=rt)
+    torch.cuda.synchronize()
+    n = int(ref["offsets"][-1])
+    assert_close(f64(yp[:n]), ref["y_perm"], wl.dtype, "y_perm")
+
+
+# ---------------------------------------------------------------------------
+# a token naming the same expert twice (pre-routed input can; top-k never does)
+# ---------------------------------------------------------------------------
+
+def _repeated_ids(T, E, k, seed):
+    r = np.random.default_rng(seed)
+    ids = r.integers(-1, E, (T, k)).astype(np.int32)     # repeats and skipped slots
+    ids[0] = 2                                           # every slot the same expert
+    if T >= 3:
+        ids[1, :3] = [1, -1, 1]
+        ids[T - 1] = -1                                  # no slot at all
+    return ids
+
+
+@pytest.mark.parametrize("T,E,k", [(700, 9, 4), (300, 8, 8), (1, 4, 4)])
+def test_permute_repeated_ids_follow_the_counting_sort(T, E, k):
+    ids = _repeated_ids(T, E, k, seed=T + E)
+    gen = torch.Generator(device=DEV).manual_seed(2)
+    x = torch.randn(T, 64, generator=gen, device=DEV).to(torch.bfloat16)
+    off, rt, sr, xp = B.moe_permute(x, torch.from_numpy(ids).to(DEV), E)
+    torch.cuda.synchronize()
+    r_off, r_rt, r_sr = orc.permute(ids, E)
+    N = int(r_off[-1])
+    assert np.array_equal(i64(off), r_off)
+    got_rt = i64(rt)[:N]
+    assert np.array_equal(got_rt, r_rt) and got_rt.min(initial=0) >= 0 and got_rt.max(initial=0) < T
+    assert np.array_equal(i64(sr), r_sr)
+    assert bits_equal(xp[:N], x[torch.from_numpy(r_rt.astype(np.int64)).to(DEV)])
+
+
+def test_pre_routed_layer_with_repeated_ids():
+    T, d, E, k, F = 700, 128, 9, 4, 192
+    ids = _repeated_ids(T, E, k, seed=5)
+    r = np.random.default_rng(6)
+    w = r.random((T, k)).astype(np.float32)
+    w[ids < 0] = 0.0
+    gen = torch.Generator(device=DEV).manual_seed(7)
+    x = torch.randn(T, d, generator=gen, device=DEV).to(torch.bfloat16)
+    wg = (torch.randn(E, F, d, generator=gen, device=DEV) / d ** 0.5).to(torch.bfloat16)
+    wu = (torch.randn(E, F, d, generator=gen, device=DEV) / d ** 0.5).to(torch.bfloat16)
+    wd = (torch.randn(E, d, F, generator=gen, device=DEV) / F ** 0.5).to(torch.bfloat16)
+    L = B.moe_layer_forward(x, None, None, wg, wu, wd, k, topk_ids=torch.from_numpy(ids).to(DEV),
+                            topk_w=torch.from_numpy(w).to(DEV), want_offsets=True)
+    torch.cuda.synchronize()
+    ref = orc.layer_forward(f64(x), None, None, LazyExperts(wg), LazyExperts(wu), LazyExperts(wd), k, ids=ids,
+                            weights=w)
+    assert np.array_equal(i64(L.offsets), ref["offsets"])
+    assert_close(f64(L.y), ref["y"], torch.bfloat16, "y")

@@ -141,6 +141,15 @@ def _m_grouped_skip_last_expert(m):
     m.grouped_ffn = grouped_ffn
 
 
+def _m_bf16_bits_misread(m):
+    def to_f64(a):
+        a = np.asarray(a)
+        if a.dtype == np.uint16:                  # read as IEEE half instead of bf16
+            return a.view(np.float16).astype(np.float64)
+        return a.astype(np.float64)
+    m.to_f64 = to_f64
+
+
 MUTATIONS = [v for k, v in sorted(globals().items()) if k.startswith("_m_")]
 
 
