@@ -191,6 +191,26 @@ moe_status moe_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
                              int32_t* offsets_out, void* ws, size_t* ws_bytes, void* stream);
 
 /*
+ * moe_layer_forward_noalloc: moe_layer_forward without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Its workspace is a device
+ * array inside this library of MOE_NOALLOC_SCRATCH_BYTES bytes, which every GPU
+ * the library runs on holds until the process ends; a call whose workspace query
+ * (moe_layer_forward with ws == NULL) exceeds it returns MOE_ERR_WORKSPACE before
+ * anything is launched.  At the page's layer shape (d 6,144, E 384, top-8, F
+ * 1,792, bf16) that is up to 521 routed tokens per call.  Same kernels and results as
+ * moe_layer_forward; it calls no allocator.  Calls that overlap on one GPU share
+ * the array and race: order them on one stream (or synchronise between them).
+ * Arguments and errors as moe_layer_forward.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_layer_forward_noalloc(int64_t T, int64_t d, int64_t E, int64_t k, int64_t F, moe_dtype dtype,
+                                     const void* x, const void* w_router, const float* bias,
+                                     const void* w_gate, const void* w_up, const void* w_down,
+                                     void* y, float* logits_out, int32_t* topk_ids, float* topk_w,
+                                     int32_t* offsets_out, void* stream);
+
+/*
  * moe_grouped_ffn_backward: gradients of the grouped SwiGLU FFN (the layer
  * backward's matrix products; the pages' workload is pre-training, "Training a
  * 1T-Parameter MoE on EU public infrastructure with PyTorch and TorchTitan").

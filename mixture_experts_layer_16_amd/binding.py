@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_F32, MOE_BF16 = 0, 1
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
 EXPORTS = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward", "moe_newton_schulz",
-           "moe_grouped_ffn_backward", "moe_combine_backward", "moe_route_backward", "moe_layer_backward")
+           "moe_grouped_ffn_backward", "moe_combine_backward", "moe_route_backward", "moe_layer_backward",
+           "moe_layer_forward_noalloc")
 
 
 class MoEError(RuntimeError):
@@ -40,6 +41,8 @@ _SIGS = {
     "moe_combine": [_i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp],
     "moe_layer_forward": [_i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                           _vp, _vp, _szp, _vp],
+    "moe_layer_forward_noalloc": [_i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, _vp],
     "moe_newton_schulz": [_i64, _i64, _i64, _int, _i64, _f32, _f32, _f32, _f32, _vp, _vp, _vp, _szp, _vp],
     "moe_grouped_ffn_backward": [_i64, _i64, _i64, _i64, _int, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _vp, _vp, _vp, _szp, _vp],

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["route.hip", "permute.hip", "grouped_ffn.hip", "combine.hip", "newton_schulz.hip", "ffn_backward.hip", "layer_backward.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "permute.hip", "grouped_ffn.hip", "combine.hip", "newton_schulz.hip", "ffn_backward.hip", "layer_backward.hip", "noalloc.hip", "moe_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

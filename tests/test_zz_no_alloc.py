@@ -1,0 +1,82 @@
+"""moe_layer_forward_noalloc (the layer forward with its workspace in the
+library's own device array, for callers that cannot allocate) against
+moe_layer_forward on the same inputs: the same kernels and workspace layout, so
+every output must be the same bits.  Two calls in a row, the second smaller, so
+the array is reused with a different layout; a request above the array's size is
+refused on the host before anything is launched."""
+import ctypes
+
+import pytest
+import torch
+
+from mixture_experts_layer_16_amd import binding as B
+from mixture_experts_layer_16_amd import workloads as W
+from parity_util import bits_equal
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _fn():
+    return B.lib().moe_layer_forward_noalloc
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _noalloc(inp, wl, routed):
+    T, d, E, k, F = wl.T, wl.d, wl.E, wl.k, wl.F
+    y = torch.empty(T, d, dtype=wl.dtype, device=DEV)
+    off = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    if routed:
+        ids = torch.empty(T, k, dtype=torch.int32, device=DEV)
+        w = torch.empty(T, k, dtype=torch.float32, device=DEV)
+        logits = torch.empty(T, E, dtype=torch.float32, device=DEV)
+    else:
+        ids, w, logits = inp["topk_ids"], inp["topk_w"], None
+    st = _fn()(T, d, E, k, F, B.dtype_code(wl.dtype), _p(inp["x"]), _p(inp["w_router"]), _p(inp["bias"]),
+               _p(inp["w_gate"]), _p(inp["w_up"]), _p(inp["w_down"]), _p(y), _p(logits), _p(ids), _p(w), _p(off),
+               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, st
+    return y, logits, ids, w, off
+
+
+def _compare(wl, seed):
+    inp = W.make_inputs(wl, device=DEV, seed=seed)
+    routed = inp["w_router"] is not None
+    print(f"[noalloc] {wl.name}: T={wl.T} d={wl.d} E={wl.E} k={wl.k} F={wl.F} routed={routed}", flush=True)
+    L = B.moe_layer_forward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"], inp["w_down"], wl.k,
+                            topk_ids=inp.get("topk_ids"), topk_w=inp.get("topk_w"), want_logits=routed,
+                            want_routing=routed, want_offsets=True)
+    y, logits, ids, w, off = _noalloc(inp, wl, routed)
+    torch.cuda.synchronize()
+    assert bits_equal(y, L.y)
+    assert torch.equal(off, L.offsets)
+    if routed:
+        assert bits_equal(logits, L.logits) and torch.equal(ids, L.topk_ids) and bits_equal(w, L.topk_w)
+
+
+CASES = [
+    # about 51 MB of workspace, then a much smaller layout in the same array
+    (W.Workload("noalloc_big", T=2048, d=1024, E=64, k=8, F=512, dtype=torch.bfloat16), 0),
+    (W.Workload("noalloc_small", T=300, d=256, E=16, k=4, F=128, dtype=torch.bfloat16, routing="router_bias"), 1),
+]
+
+
+def test_noalloc_matches_layer_forward_twice_second_smaller():
+    for wl, seed in CASES:
+        _compare(wl, seed)
+
+
+def test_noalloc_pre_routed_and_fp32():
+    _compare(W.Workload("noalloc_pre", T=900, d=128, E=12, k=4, F=192, dtype=torch.bfloat16, routing="pre_routed",
+                        n_slots=1500, n_empty=2, hot_frac=0.3), 2)
+    _compare(W.WORKLOADS["tiny_fp32"], 0)
+
+
+def test_noalloc_refuses_more_than_its_array():
+    # the page's layer shape at 65,536 tokens needs about 8.3 GB: refused on the host
+    P = ctypes.c_void_p(0x10000)
+    st = _fn()(65536, 6144, 384, 8, 1792, 1, P, P, None, P, P, P, P, None, None, None, None, None)
+    assert st == 3
