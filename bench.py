@@ -9,8 +9,17 @@ sequence with Zipf-like routing skew.
 Prints one JSON line.  `roofline` covers the grouped FFN (its gate/up and down
 GEMM launches, timed together with HIP events on the launch stream) against
 the bf16 dense MFMA peak; `stages_ms` gives each step's average duration from
-a second, stage-by-stage pass; `cpu_baseline` times the float64 CPU oracle on a
-bounded slice of the same workload.
+a second, stage-by-stage pass; `kernels` gives every kernel's average device
+time from a third pass traced with torch's profiler (HIP activity records), and
+each kernel's fraction of its roofline (MFMA peak for the GEMMs, HBM peak for
+route's top-k, permute and combine); `other_workloads` times the 8,192-token
+balanced workload and the expert-parallel rank's share the same way;
+`cpu_baseline` times the float64 CPU oracle, step by step, on a bounded slice of
+the same workload, and `cpu_oracle` on the whole small workload.
+
+`--cpu-only NAME[,NAME...]` times only the oracle, step by step, on whole
+workloads (inputs drawn on the GPU, copied to the host) and prints one JSON line
+per workload.
 
 `--path backward` measures the layer backward (moe_layer_backward: combine,
 grouped expert FFN, gate-weight/router and permutation backward) from the
@@ -52,6 +61,10 @@ def parse():
                     help="newton_schulz: experts whose gate, up and down matrices one step orthogonalises")
     ap.add_argument("--cpu-tokens", type=int, default=512,
                     help="tokens of the workload the CPU oracle runs on (0 = skip)")
+    ap.add_argument("--other-workloads", default="page_balanced,ep_rank_share",
+                    help="workloads timed after the main one (comma-separated; empty: none)")
+    ap.add_argument("--cpu-only", default="",
+                    help="comma-separated workloads: time only the CPU oracle on each whole workload")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run one 1 GiB device copy, then one grouped FFN call, and exit "
                          "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
@@ -129,34 +142,230 @@ def stage_pass(torch, B, inp, wl, steps):
     return {n: v / steps for n, v in acc.items()}
 
 
+def host_info():
+    """CPU model, core count and the BLAS library numpy's products run on."""
+    from threadpoolctl import threadpool_info
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in blas] + [1])
+    lib = ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in blas) or "unknown"
+    return {"cpu_model": model, "host_cpus": os.cpu_count(), "blas": lib, "blas_threads": threads}
+
+
+def oracle_stages(orc, x, wr, b, wg, wu, wd, k, ids=None, weights=None):
+    """The oracle's own steps in layer_forward's order, each timed (seconds)."""
+    t = {}
+    t0 = time.perf_counter()
+    if ids is None:
+        logits = orc.router_logits(x, wr, b)
+        ids, w = orc.select_topk(logits, k)
+    else:
+        w = orc.to_f64(weights)
+    t1 = time.perf_counter()
+    offsets, row_token, slot_row = orc.permute(ids, len(wg))
+    x_perm = orc.gather_rows(x, row_token)
+    t2 = time.perf_counter()
+    y_perm = orc.grouped_ffn(x_perm, offsets, wg, wu, wd)
+    t3 = time.perf_counter()
+    orc.combine(y_perm, slot_row, w)
+    t4 = time.perf_counter()
+    if wr is not None:
+        t["route"] = t1 - t0
+    t.update(permute=t2 - t1, expert_ffn=t3 - t2, combine=t4 - t3, layer=t4 - t0)
+    return t, int(offsets[-1])
+
+
+class _HostExperts:
+    """Per-expert weights on the host as stored: bf16 as uint16 bit patterns
+    (the oracle widens one expert at a time), float32 as it is."""
+
+    def __init__(self, torch, t, progress=""):
+        import numpy as np
+        self.h = t.cpu()
+        self.bits = t.dtype == torch.bfloat16
+        self.np, self.torch = np, torch
+        self.progress = progress
+
+    def __len__(self):
+        return self.h.shape[0]
+
+    def __getitem__(self, e):
+        if self.progress and e % 48 == 0:
+            print(f"[{self.progress}] expert {e} of {len(self)}", file=sys.stderr, flush=True)
+        if self.bits:
+            return self.h[e].view(self.torch.int16).numpy().view(self.np.uint16)
+        return self.h[e].numpy()
+
+
+def _host_tokens(torch, t):
+    """Token rows on the host as stored (bf16 as uint16 bit patterns)."""
+    import numpy as np
+    t = t.cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def cpu_oracle_run(torch, inp, wl, n_tokens, repeats=1, progress=""):
+    """The float64 oracle step by step on the first n_tokens tokens (0 = all) of
+    the workload's inputs; the median run of `repeats`."""
+    import numpy as np
+    from oracle import moe_oracle as orc
+    n = wl.T if n_tokens <= 0 else min(n_tokens, wl.T)
+    x = _host_tokens(torch, inp["x"][:n])
+    routed = inp["w_router"] is not None
+    wr = _host_tokens(torch, inp["w_router"]) if routed else None
+    b = inp["bias"].cpu().numpy() if inp.get("bias") is not None else None
+    ew = [_HostExperts(torch, inp[k], progress if k == "w_gate" else "") for k in ("w_gate", "w_up", "w_down")]
+    kw = {} if routed else dict(ids=inp["topk_ids"][:n].cpu().numpy(), weights=inp["topk_w"][:n].cpu().numpy())
+    runs = []
+    for _ in range(repeats):
+        t, slots = oracle_stages(orc, x, wr, b, *ew, wl.k, **kw)
+        runs.append(t)
+    runs.sort(key=lambda r: r["layer"])
+    t = runs[len(runs) // 2]
+    flops = 6.0 * slots * wl.d * wl.F + (2.0 * n * wl.d * wl.E if routed else 0.0)
+    return n, slots, t, flops
+
+
 def cpu_baseline(torch, inp, wl, n_tokens):
     """The float64 oracle on the first n_tokens tokens of the workload (their
-    routing, permutation, every expert FFN they use, and the combine)."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
-    from oracle import moe_oracle as orc
+    routing, permutation, every expert FFN they use, and the combine), step by
+    step."""
+    info = host_info()
+    n, slots, t, flops = cpu_oracle_run(torch, inp, wl, n_tokens)
+    return {"value": round(n / t["layer"], 3), "unit": "tokens/s", "cores": info["blas_threads"], "kind": "oracle",
+            "sample": f"first {n} of {wl.T} tokens of {wl.name} ({slots} slots): the float64 oracle's steps "
+                      f"(routing, permutation, SwiGLU FFN of every expert they use, combine) in "
+                      f"{t['layer']:.1f} s on {info['blas_threads']} BLAS threads of {info['host_cpus']} host CPUs",
+            "stages_s": {k_: round(v, 4) for k_, v in t.items()},
+            "gflops": round(flops / t["layer"] / 1e9, 2), **info}
 
-    f64 = lambda t: None if t is None else t.detach().to("cpu").to(torch.float64).numpy()
-    n = min(n_tokens, wl.T)
-    x = f64(inp["x"][:n])
-    routed = inp["w_router"] is not None
-    host = {k: inp[k].cpu() for k in ("w_gate", "w_up", "w_down")}   # bf16 on the host, as stored
-    to_np = lambda t: (t.view(torch.int16).numpy().view(np.uint16))  # bf16 bits; the oracle widens them
-    wg = [to_np(host["w_gate"][e]) for e in range(wl.E)]
-    wu = [to_np(host["w_up"][e]) for e in range(wl.E)]
-    wd = [to_np(host["w_down"][e]) for e in range(wl.E)]
-    kw = {}
-    if not routed:
-        kw = dict(ids=inp["topk_ids"][:n].cpu().numpy(), weights=inp["topk_w"][:n].cpu().numpy())
-    wr, b = f64(inp["w_router"]), f64(inp["bias"])
-    t0 = time.perf_counter()
-    orc.layer_forward(x, wr, b, wg, wu, wd, wl.k, **kw)
-    dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {wl.T} tokens of {wl.name}: float64 oracle end to end (routing, "
-                      f"permutation, SwiGLU FFN of every expert they use, combine); {dt:.1f} s on "
-                      f"{threads} BLAS threads of {os.cpu_count()} host CPUs"}
+
+def cpu_only(args, torch, W):
+    """Time the oracle, step by step, on whole workloads (one JSON line each)."""
+    info = host_info()
+    for name in [w for w in args.cpu_only.split(",") if w]:
+        wl = W.WORKLOADS[name]
+        inp = W.make_inputs(wl, device="cuda:0")
+        reps = 3 if wl.T * wl.k * wl.d * wl.F <= 4096 * 8 * 1024 * 512 else 1
+        n, slots, t, flops = cpu_oracle_run(torch, inp, wl, 0, repeats=reps, progress=name)
+        del inp
+        torch.cuda.empty_cache()
+        print(json.dumps({"cpu_oracle": name, "tokens": n, "slots": slots, "runs": reps,
+                          "note": "float64 oracle (numpy), the median of the runs" if reps > 1 else
+                                  "float64 oracle (numpy), one run",
+                          "stages_s": {k_: round(v, 4) for k_, v in t.items()},
+                          "tokens_per_s": round(n / t["layer"], 3), "gflops": round(flops / t["layer"] / 1e9, 2),
+                          **info}), flush=True)
+
+
+def kernel_split(torch, L, routed, reps=3):
+    """Average device time (ms) of every kernel of one layer call, from torch's
+    profiler (HIP activity records of the library's launches)."""
+    from torch.profiler import ProfilerActivity, profile
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        for _ in range(reps):
+            L()
+        torch.cuda.synchronize()
+    evs = [e for e in prof.events() if e.device_type == torch.autograd.DeviceType.CUDA]
+    evs.sort(key=lambda e: e.time_range.start)
+    gemms = (["router_gemm"] if routed else []) + ["gate_up_gemm", "down_gemm"]
+    acc, gi = {}, 0
+    for e in evs:
+        n = e.name
+        if "grouped_gemm_kernel" in n:
+            role = gemms[gi % len(gemms)]
+            gi += 1
+        elif "topk" in n:
+            role = "topk"
+        elif "permute" in n:
+            role = "permute"
+        elif "combine_kernel" in n:
+            role = "combine"
+        else:
+            continue
+        us = e.device_time if hasattr(e, "device_time") else e.cuda_time
+        acc[role] = acc.get(role, 0.0) + us
+    if gi != reps * len(gemms):
+        raise RuntimeError(f"profiler saw {gi} GEMM launches, expected {reps * len(gemms)}")
+    return {k_: v / reps / 1e3 for k_, v in acc.items()}
+
+
+def kernel_fractions(wl, es, km):
+    """Each kernel's algorithmic work per launch over its measured time, as a
+    fraction of its roofline.  Bytes count every tensor read or written once."""
+    import math
+    nblk = math.ceil(wl.T / 256)
+    out = {}
+    def mfma(name, flops):
+        if name in km:
+            out[name] = {"ms": round(km[name], 4), "tflops": round(flops / km[name] / 1e9, 1),
+                         "mfma_frac": round(flops / km[name] / 1e9 / PEAK_BF16_TFLOPS, 4), "flops": flops}
+    def hbm(name, nbytes):
+        if name in km:
+            out[name] = {"ms": round(km[name], 4), "gbs": round(nbytes / km[name] / 1e6, 1),
+                         "hbm_frac": round(nbytes / km[name] / 1e6 / PEAK_HBM_GBS, 4), "bytes": nbytes}
+    if wl.routing != "pre_routed":
+        mfma("router_gemm", 2.0 * wl.T * wl.d * wl.E)
+        out["router_gemm"]["bytes"] = wl.T * wl.d * es + wl.E * wl.d * es + wl.T * wl.E * 4
+        hbm("topk", wl.T * wl.E * 4 + wl.T * wl.k * 8)
+    # ids read twice; block counts written, scanned and read; row_token and slot_row written
+    hbm("permute", wl.T * wl.k * 4 * 2 + nblk * wl.E * 4 * 4 + (wl.E + 1) * 4 + wl.N * 4 + wl.T * wl.k * 4)
+    mfma("gate_up_gemm", 4.0 * wl.N * wl.d * wl.F)
+    mfma("down_gemm", 2.0 * wl.N * wl.d * wl.F)
+    hbm("combine", wl.N * wl.d * es + wl.T * wl.d * es + wl.T * wl.k * 8)
+    return out
+
+
+def time_layer(torch, L, steps):
+    """Mean ms per call of L over `steps` calls, one event before and after."""
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        L()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def other_workload(torch, B, W, name, steps, warmup):
+    """The layer forward on another workload: tokens/s, the grouped FFN's MFMA
+    fraction and (weight-streaming case) its fraction of the HBM floor."""
+    wl = W.WORKLOADS[name]
+    inp = W.make_inputs(wl, device="cuda:0")
+    L = B.LayerForward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"], inp["w_down"], wl.k,
+                       topk_ids=inp.get("topk_ids"), topk_w=inp.get("topk_w"))
+    for _ in range(warmup):
+        L()
+    ms = time_layer(torch, L, steps)
+    stages = stage_pass(torch, B, inp, wl, 3)
+    es = 2 if wl.dtype == torch.bfloat16 else 4
+    ffn = stages["grouped_ffn"]
+    tflops = wl.expert_flops() / (ffn / 1e3) / 1e12
+    # the grouped FFN's minimum HBM traffic: every expert's weights once, its input
+    # rows read, h written and read, y_perm written
+    wbytes = 3.0 * wl.E * wl.d * wl.F * es
+    act = wl.N * (wl.d * es * 2 + wl.F * es * 2)
+    floor_ms = max(wl.expert_flops() / PEAK_BF16_TFLOPS / 1e9, (wbytes + act) / PEAK_HBM_GBS / 1e6)
+    out = {"tokens_per_s": round(wl.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4), "steps": steps,
+           "tokens": wl.T, "experts": wl.E, "slots": wl.N, "routing": wl.routing,
+           "grouped_ffn_ms": round(ffn, 4), "grouped_ffn_tflops": round(tflops, 1),
+           "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+           "roofline_floor_ms": round(floor_ms, 4), "frac_of_roofline_floor": round(floor_ms / ffn, 4),
+           "stages_ms": {k_: round(v, 4) for k_, v in stages.items()}}
+    del L, inp
+    torch.cuda.empty_cache()
+    return out
 
 
 NS_METRIC = "Muon Newton-Schulz expert matrices/s (5 quintic steps, d6144 x F1792, bf16)"
@@ -354,6 +563,9 @@ def main():
     if args.path == "backward":
         bench_backward(args, torch, B, W)
         return
+    if args.cpu_only:
+        cpu_only(args, torch, W)
+        return
     wl = W.WORKLOADS[args.workload]
     if args.traffic_probe:
         traffic_probe(torch, B, W, wl)
@@ -386,8 +598,16 @@ def main():
     traffic = None
     if TRAFFIC and TRAFFIC["kernel_source_hash"] == kernel_source_hash() and TRAFFIC["workload"] == wl.name:
         traffic = TRAFFIC["bytes"]
-    perm_bytes = wl.T * wl.k * 4 * 3                  # indices only: ids read, slot_row and row_token written
-    comb_bytes = wl.N * wl.d * es + wl.T * wl.d * es + wl.T * wl.k * 8
+    try:
+        km = kernel_split(torch, L, inp["w_router"] is not None)
+        kernels = kernel_fractions(wl, es, km)
+    except Exception as exc:          # the profiler is a measurement aid, not the product
+        kernels = {"error": f"{type(exc).__name__}: {exc}"}
+    route = None
+    if "router_gemm" in kernels and "topk" in kernels:
+        route = {"router_gemm_ms": kernels["router_gemm"]["ms"], "router_mfma_frac": kernels["router_gemm"]["mfma_frac"],
+                 "topk_ms": kernels["topk"]["ms"], "topk_hbm_frac": kernels["topk"]["hbm_frac"],
+                 "route_ms": round(stages["route"], 4)}
 
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -403,11 +623,27 @@ def main():
         "tflops_layer": round(total_tflops, 1),
         "step_ms": {"median": round(per_step[len(per_step) // 2], 4), "min": round(per_step[0], 4)},
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
-        "hbm_frac": {"permute": round(perm_bytes / (stages["permute"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
-                     "combine": round(comb_bytes / (stages["combine"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "route": route,
+        "kernels": kernels,
     }
     if args.cpu_tokens > 0:
         out["cpu_baseline"] = cpu_baseline(torch, inp, wl, args.cpu_tokens)
+    del L, inp
+    torch.cuda.empty_cache()
+    others = {}
+    for name in [w for w in args.other_workloads.split(",") if w and w != wl.name]:
+        others[name] = other_workload(torch, B, W, name, min(args.steps, 10), max(1, min(args.warmup, 3)))
+    if others:
+        out["other_workloads"] = others
+    if args.cpu_tokens > 0:
+        small = W.WORKLOADS["small_bf16"]
+        sinp = W.make_inputs(small, device="cuda:0")
+        n, slots, t, flops = cpu_oracle_run(torch, sinp, small, 0, repeats=3)
+        out["cpu_oracle"] = {"small_bf16": {"tokens": n, "slots": slots, "runs": 3,
+                                            "stages_s": {k_: round(v, 4) for k_, v in t.items()},
+                                            "tokens_per_s": round(n / t["layer"], 2),
+                                            "gflops": round(flops / t["layer"] / 1e9, 2)}}
+        del sinp
     print(json.dumps(out), flush=True)
 
 
