@@ -354,6 +354,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   constexpr int KSUB = Cfg::kSub;
   static_assert(PD >= 1 && PD < KSUB, "prefetch distance must be 1 .. sub-steps - 1");
   constexpr bool GRP = (FEAT & kFeatGroups) != 0, STR = (FEAT & kFeatStrides) != 0;
+  // only the SwiGLU epilogues' GEMMs (the expert FFN's first product, forward and
+  // backward recompute) read A through a gather map; the others ignore a_rows
+  constexpr bool kMayGather = paired_epilogue(EPI);
   constexpr bool BKN = (FEAT & kFeatBKN) != 0;
   static_assert(!BKN || (sizeof(T) == 2 && !paired_epilogue(EPI) && !STR && Cfg::kSub * 16 == BK && BN % 128 == 0),
                 "B along N: 16-bit elements, one B per output column block, BN a multiple of 128");
@@ -437,7 +440,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     for (int i = 0; i < CPA; ++i) {
       const int row = (i * NT + tid) * 16 / RB;
       const int r = min(row, t.rows_valid - 1);              // rows past the segment: any valid row
-      arow[i] = p.a_rows ? clamp_row(p.a_rows[t.m0 + r], p.a_rows_n) : r;
+      arow[i] = (kMayGather && p.a_rows) ? p.a_rows[t.m0 + r] : r;   // clamped where used (setup), so the
+                                                   // loads' wait lands there, not here
     }
   };
 
@@ -450,7 +454,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
   auto setup = [&](const TileInfo& t, const int* arow) {
     const int64_t k0 = STR ? t.k0 : 0;
     const int64_t ka0 = (STR && p.ksa) ? k0 / BK * p.ksa : k0, kb0 = (STR && p.ksb) ? k0 / BK * p.ksb : k0;
-    Ab = reinterpret_cast<const char*>(Abase + ka0 + (p.a_rows ? 0 : ((STR && p.a_shared) ? t.mrel : t.m0) * lda));
+    Ab = reinterpret_cast<const char*>(Abase + ka0 +
+                                       ((kMayGather && p.a_rows) ? 0 : ((STR && p.a_shared) ? t.mrel : t.m0) * lda));
     if constexpr (BKN) {
       // [K, N]: the tile's columns start n0 elements into every k row
       Bgb = reinterpret_cast<const char*>(static_cast<const T*>(p.B0) + (int64_t)t.g * p.b_stride + t.n0);
@@ -479,7 +484,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
       const int lc = Cfg::swz(row, (byte % RB) / 16);
       int r;
       if (i < CPA) {
-        r = arow[i];
+        r = (kMayGather && p.a_rows) ? clamp_row(arow[i], p.a_rows_n) : arow[i];
       } else {
         const int br = row - BM;
         const int half = paired_epilogue(EPI) ? BN / 2 : BN;
@@ -848,17 +853,27 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     if (STAGES - 2 <= nk - 1) wait_vmcnt<(STAGES - 2) * CPT>();
     else wait_vmcnt<0>();
     block_barrier();
-    // look up the next tile now, before the next stage's copies go out: the
-    // compiler waits for its own loads with a full memory-counter wait, which
-    // would also wait for copies issued ahead of them.  Its row numbers arrive
-    // during this K loop.
+    // Look up the next tile.  With a gather map, before the next stage's copies
+    // go out: the compiler waits for its own loads (the row numbers) with a full
+    // memory-counter wait, which would also wait for copies issued ahead of them;
+    // the row numbers then arrive during this K loop.  Without one the lookup only
+    // reads LDS, so the copies go out first and the lookup runs under them.
+    // (Only the SwiGLU epilogues' GEMMs read A through a gather map.)
     const int next_tile = tile + step;
     const bool more = next_tile < end;
-    if (more) {
-      nxt = locate(next_tile);
-      fetch_rows(nxt, arow_n);
+    if constexpr (kMayGather) {
+      if (more) {
+        nxt = locate(next_tile);
+        fetch_rows(nxt, arow_n);
+      }
+      if (STAGES - 1 < nk) load_stage((STAGES - 1) % STAGES, STAGES - 1);
+    } else {
+      if (STAGES - 1 < nk) load_stage((STAGES - 1) % STAGES, STAGES - 1);
+      if (more) {
+        nxt = locate(next_tile);
+        fetch_rows(nxt, arow_n);
+      }
     }
-    if (STAGES - 1 < nk) load_stage((STAGES - 1) % STAGES, STAGES - 1);
       // the K loop, compiled twice: without per-block checks for tiles whose row
     // blocks are all live, with them for ragged tiles (the checks cost the
     // compiler its exact tracking of outstanding LDS reads)
