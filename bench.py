@@ -63,6 +63,8 @@ def parse():
                     help="tokens of the workload the CPU oracle runs on (0 = skip)")
     ap.add_argument("--other-workloads", default="page_balanced,ep_rank_share",
                     help="workloads timed after the main one (comma-separated; empty: none)")
+    ap.add_argument("--no-kernel-split", action="store_true",
+                    help="skip the per-kernel pass traced with torch's profiler (for runs under rocprofv3)")
     ap.add_argument("--cpu-only", default="",
                     help="comma-separated workloads: time only the CPU oracle on each whole workload")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -75,10 +77,10 @@ def parse():
 # of the page shape, from rocprofv3 FETCH_SIZE and WRITE_SIZE runs of
 # `bench.py --traffic-probe`, each scaled by the same counter's reading for a
 # 1 GiB device copy.  Valid only for the kernel sources it was measured on.
-TRAFFIC = {"workload": "page_seq64k_skewed", "kernel_source_hash": "11923f4b7f7d288c", "bytes": 103722648169,
+TRAFFIC = {"workload": "page_seq64k_skewed", "kernel_source_hash": "cec77d931084544e", "bytes": 106139941449,
            "fetch_scale": 1.9999, "write_scale": 1.0000}
 KERNEL_SOURCES = ["mixture_experts_layer_16_amd/csrc/gemm_tile.h", "mixture_experts_layer_16_amd/csrc/grouped_ffn.hip",
-                  "mixture_experts_layer_16_amd/csrc/common.h"]
+                  "mixture_experts_layer_16_amd/csrc/common.h", "mixture_experts_layer_16_amd/csrc/tile_walk.h"]
 
 
 def kernel_source_hash() -> str:
@@ -598,11 +600,14 @@ def main():
     traffic = None
     if TRAFFIC and TRAFFIC["kernel_source_hash"] == kernel_source_hash() and TRAFFIC["workload"] == wl.name:
         traffic = TRAFFIC["bytes"]
-    try:
-        km = kernel_split(torch, L, inp["w_router"] is not None)
-        kernels = kernel_fractions(wl, es, km)
-    except Exception as exc:          # the profiler is a measurement aid, not the product
-        kernels = {"error": f"{type(exc).__name__}: {exc}"}
+    if args.no_kernel_split:
+        kernels = {"skipped": "--no-kernel-split"}
+    else:
+        try:
+            km = kernel_split(torch, L, inp["w_router"] is not None)
+            kernels = kernel_fractions(wl, es, km)
+        except Exception as exc:          # the profiler is a measurement aid, not the product
+            kernels = {"error": f"{type(exc).__name__}: {exc}"}
     route = None
     if "router_gemm" in kernels and "topk" in kernels:
         route = {"router_gemm_ms": kernels["router_gemm"]["ms"], "router_mfma_frac": kernels["router_gemm"]["mfma_frac"],
