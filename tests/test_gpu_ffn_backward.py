@@ -100,10 +100,12 @@ def test_ffn_backward_gather_equals_x_perm():
         assert torch.equal(a[i], b[i])
 
 
-def test_ffn_backward_page_shape_sampled():
-    # the page's layer shape at 65,536 tokens with its skewed routing: dX on
-    # sampled rows of the largest expert, full weight gradients of the two
-    # smallest non-empty experts
+def test_ffn_backward_page_shape_largest_expert_in_full():
+    # the page's layer shape at 65,536 tokens with its skewed routing: every dX row
+    # and all three weight gradients of the largest expert (about 27,800 rows: its
+    # weight-gradient tiles contract over ~434 k-tiles, its dX/dH tiles walk many
+    # chunks of row tiles), and full weight gradients of the two smallest non-empty
+    # experts (a k range of one or two k-tiles)
     wl = W.WORKLOADS["page_seq64k_skewed"]
     print(f"[bwd] page shape T={wl.T} d={wl.d} E={wl.E} F={wl.F}", flush=True)
     inp = W.make_inputs(wl, device=DEV)
@@ -116,21 +118,17 @@ def test_ffn_backward_page_shape_sampled():
     torch.cuda.synchronize()
     offs = off.cpu().numpy().astype(np.int64)
     counts = np.diff(offs)
-    rng = np.random.default_rng(5)
-    big = int(np.argmax(counts))
-    lo, hi = offs[big], offs[big + 1]
-    S = np.unique(np.concatenate([[lo, hi - 1], rng.integers(lo, hi, 30)]))
-    St = torch.from_numpy(S).to(DEV)
-    X = f64(inp["x"][rt[St].long()])
-    ref = bo.expert_ffn_backward(X, f64(inp["w_gate"][big]), f64(inp["w_up"][big]), f64(inp["w_down"][big]),
-                                 f64(dy[St]))
-    close_scaled(f64(dx[St]), ref[0], "dx rows of the largest expert")
     nz = np.nonzero(counts)[0]
-    for e in nz[np.argsort(counts[nz])[:2]]:
+    big = int(np.argmax(counts))
+    for e in [big] + [int(v) for v in nz[np.argsort(counts[nz])[:2]]]:
         lo, hi = offs[e], offs[e + 1]
+        print(f"[bwd] expert {e}: {hi - lo} rows in full", flush=True)
         idx = torch.arange(lo, hi, device=DEV)
         ref = bo.expert_ffn_backward(f64(inp["x"][rt[idx].long()]), f64(inp["w_gate"][e]), f64(inp["w_up"][e]),
                                      f64(inp["w_down"][e]), f64(dy[idx]))
+        if e == big:
+            close_scaled(f64(dx[idx]), ref[0], f"dX, every row of expert {e}")
         close_scaled(f64(dwg[e]), ref[1], f"dW_gate[{e}]")
         close_scaled(f64(dwu[e]), ref[2], f"dW_up[{e}]")
         close_scaled(f64(dwd[e]), ref[3], f"dW_down[{e}]")
+        del ref
