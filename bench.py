@@ -59,8 +59,10 @@ def parse():
                          "of whole expert matrices; backward: the grouped expert-FFN backward")
     ap.add_argument("--ns-experts", type=int, default=96,
                     help="newton_schulz: experts whose gate, up and down matrices one step orthogonalises")
-    ap.add_argument("--cpu-tokens", type=int, default=512,
-                    help="tokens of the workload the CPU oracle runs on (0 = skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="tokens of the workload the CPU oracle runs on (0 = skip; default 8192 for the forward, "
+                         "1024 for the backward); the oracle's fixed cost of widening each expert it touches from "
+                         "bf16 dominates much smaller samples")
     ap.add_argument("--other-workloads", default="page_balanced,ep_rank_share",
                     help="workloads timed after the main one (comma-separated; empty: none)")
     ap.add_argument("--no-kernel-split", action="store_true",
@@ -70,7 +72,10 @@ def parse():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run one 1 GiB device copy, then one grouped FFN call, and exit "
                          "(for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.cpu_tokens is None:
+        args.cpu_tokens = 1024 if args.path == "backward" else 8192
+    return args
 
 
 # HBM traffic of one grouped-FFN call (gate/up + down launches) at 65,536 tokens
