@@ -24,13 +24,15 @@ namespace {
 
 // Tile order inside an expert: chunks of row tiles, column groups inside a chunk
 // (0 = no chunking / all columns together).  The 32 tiles an XCD runs side by side
-// then cover 16 row tiles x 2 column tiles of a large expert, so each weight k-slice
-// and each row k-slice is read by several of them from that XCD's L2 (measured at
-// 65,536 tokens: 30.9 -> 30.4 ms for the two GEMMs; 8 x 4, 16 x 4, 32 x 1 and
-// 32 x 2 blocks gave 30.7-30.9 ms).
-constexpr int kGateUpRowChunk = 16;
+// then cover 8 row tiles x 4 column tiles of a large expert, so each weight k-slice
+// and each row k-slice is read by several of them from that XCD's L2.  Measured at
+// 65,536 tokens (page shape, skewed routing), bytes read past L2 per call: 8 x 2
+// chunks 59 GB (gate/up) and 23.4 GB (down); 16 x 2 65 and 26.5 GB; 16 x 4 60 and
+// 23.6 GB; 8 x 4 62.6 and 24.7 GB; all at the same time (19.6 and 10.3 ms) and
+// shader clock (1.64-1.65 GHz).  Without chunking: 30.9 ms for the two GEMMs.
+constexpr int kGateUpRowChunk = 8;
 constexpr int kGateUpColumnGroup = 2;
-constexpr int kDownRowChunk = 16;
+constexpr int kDownRowChunk = 8;
 constexpr int kDownColumnGroup = 2;
 
 // Tile configuration: 256 x 256 output tiles, BK-deep k-slices, STAGES-deep LDS

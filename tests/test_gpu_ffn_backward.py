@@ -56,7 +56,7 @@ def make(counts, d, F, seed, gather):
 CASES = [([70, 0, 300, 1, 129], 128, 192, False), ([256, 256], 64, 64, False), ([0, 33, 0, 520], 192, 128, True),
          ([5], 128, 128, True), ([1, 1, 1, 1, 1, 1, 1], 64, 128, False),
          # experts of 4,400 and 5,000 rows: the forward-side GEMMs walk more than one
-         # chunk of 16 row tiles, and the weight gradients contract over 69 and 79
+         # chunk of 8 row tiles, and the weight gradients contract over 69 and 79
          # k-tiles of the expert's rows; every element of dX and all three dW compared
          ([4400, 0, 300, 37], 256, 128, True), ([5000, 3], 64, 192, False)]
 

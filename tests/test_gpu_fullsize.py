@@ -4,7 +4,7 @@ configuration that bench.py times (moe_layer_forward).  The oracle checks:
     oracle selects on the GPU's logits; the logits themselves on a token sample;
   * the expert offsets, bit-exact;
   * the grouped FFN (stage entry points) on EVERY row of the largest expert's
-    first two chunks of 16 row tiles and of its last chunk (the tile order walks
+    first two chunks of 8 row tiles and of its last chunk (the tile order walks
     a large expert chunk by chunk), and on sampled rows of the smallest non-empty
     expert and two random ones;
   * the layer output on 256 sampled tokens (plus a token with no local slot);
@@ -29,7 +29,7 @@ def expert_f64(inp, e):
     return tuple(inp[n][e].to(torch.float64).cpu().numpy() for n in ("w_gate", "w_up", "w_down"))
 
 
-ROW_CHUNK = 16 * 256   # rows of one chunk of the forward GEMMs' tile order
+ROW_CHUNK = 8 * 256    # rows of one chunk of the forward GEMMs' tile order
 
 
 @pytest.mark.parametrize("name", FULL)

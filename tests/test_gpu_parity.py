@@ -114,11 +114,12 @@ def test_permute_bit_exact(T, E, k, drop, dtype):
     ([1, 2, 300, 0, 64], 128, 64, torch.float32),
     ([1000], 512, 256, torch.bfloat16),
     ([0, 0, 7], 64, 64, torch.bfloat16),
-    # an expert past one chunk of 16 row tiles of the tile order (4,400 rows = 18 row
-    # tiles: a full chunk and a short one), odd column-tile counts in both GEMMs
+    # an expert past two chunks of 8 row tiles of the tile order (4,400 rows = 18 row
+    # tiles: two full chunks and a short one), odd column-tile counts in both GEMMs
     # (gate/up 384 / 128 = 3, down 768 / 256 = 3)
     ([4400, 0, 300, 37], 768, 384, torch.bfloat16),
-    # 20 row tiles, gate/up 192 / 128: one full and one half column tile, down one tile
+    # 20 row tiles (chunks of 8, 8, 4), gate/up 192 / 128: one full and one half
+    # column tile, down one tile
     ([5000, 0, 3], 64, 192, torch.bfloat16),
     ([4200, 5], 128, 64, torch.float32),
 ])
@@ -303,7 +304,7 @@ def test_identity_router_crafts_exact_ties(E, k, T):
 
 def test_layer_with_an_expert_past_one_row_tile_chunk():
     # Zipf routing bias over 5 experts, top-2 of 12,000 tokens: the favoured expert
-    # gets well over 16 row tiles (4,096 rows), so the grouped GEMMs walk its tiles
+    # gets well over 8 row tiles (2,048 rows), so the grouped GEMMs walk its tiles
     # in several chunks, the last one short; every output element is compared
     wl = W.Workload("long_expert", T=12000, d=256, E=5, k=2, F=384, dtype=torch.bfloat16, routing="router_bias")
     inp = _inputs(wl)
