@@ -458,10 +458,11 @@ class _ExpertBits:
 
 def bench_backward(args, torch, B, W):
     """One step: moe_layer_backward over the whole workload from the forward's
-    routing and expert outputs (computed once, beforehand, by the forward's own
-    entry points) and a seeded output gradient.  Algorithmic work of the expert
-    part 12 N d F (dH, dX, three weight gradients); its kernels also recompute G
-    and U (4 N d F more)."""
+    routing, expert outputs and kept gate/up pre-activations (computed once,
+    beforehand, by the forward's own entry points) and a seeded output gradient.
+    Algorithmic work of the expert part 12 N d F (dH, dX, three weight
+    gradients).  The same step with G and U recomputed instead (4 N d F more
+    work, no kept activations) is timed too and reported under "recompute"."""
     import numpy as np
     wl = W.WORKLOADS[args.workload]
     dev = "cuda:0"
@@ -472,7 +473,8 @@ def bench_backward(args, torch, B, W):
     else:
         ids, w = inp["topk_ids"], inp["topk_w"]
     off, rt, sr, _ = B.moe_permute(x, ids, wl.E, copy_rows=False)
-    y_perm = B.moe_grouped_ffn(x, off, wg, wu, wd, a_rows=rt, n_max=rt.numel())
+    gu = torch.empty(rt.numel(), 2 * wl.F, dtype=wl.dtype, device=dev)
+    y_perm = B.moe_grouped_ffn(x, off, wg, wu, wd, a_rows=rt, n_max=rt.numel(), gu_out=gu)
     dy = W.output_grad(wl.T, wl.d, wl.dtype, dev, seed=1)
     n = int(off[-1])
 
@@ -485,13 +487,18 @@ def bench_backward(args, torch, B, W):
         torch.cuda.synchronize()
         return start.elapsed_time(end) / reps
 
-    L = B.LayerBackward(x, wr, wg, wu, wd, ids, w, y_perm, dy)
-    for _ in range(args.warmup):
-        L()
-    torch.cuda.synchronize()
-    ms = timed(L, args.steps)
-    del L
-    torch.cuda.empty_cache()
+    def layer_ms(kept):
+        L = B.LayerBackward(x, wr, wg, wu, wd, ids, w, y_perm, dy, gu=kept)
+        for _ in range(args.warmup):
+            L()
+        torch.cuda.synchronize()
+        t = timed(L, args.steps)
+        del L
+        torch.cuda.empty_cache()
+        return t
+
+    ms = layer_ms(gu)
+    ms_recompute = layer_ms(None)
 
     # stage by stage, each on its own (same kernels as inside moe_layer_backward)
     dy_perm = torch.empty(rt.numel(), wl.d, dtype=wl.dtype, device=dev)
@@ -499,31 +506,44 @@ def bench_backward(args, torch, B, W):
     stages["permute"] = timed(lambda: B.moe_permute(x, ids, wl.E, copy_rows=False), 2)
     stages["combine_backward"] = timed(lambda: B.moe_combine_backward(dy, y_perm, sr, w, dy_perm=dy_perm), 2)
     _, gw = B.moe_combine_backward(dy, y_perm, sr, w, dy_perm=dy_perm)
-    ffn = B.GroupedFfnBackward(x, off, wg, wu, wd, dy_perm, a_rows=rt)
+    ffn = B.GroupedFfnBackward(x, off, wg, wu, wd, dy_perm, a_rows=rt, gu=gu)
     ffn()
     ffn_ms = timed(ffn, 2)
     stages["grouped_ffn_backward"] = ffn_ms
     dxp = ffn.dx
     del ffn
     torch.cuda.empty_cache()
+    ffn = B.GroupedFfnBackward(x, off, wg, wu, wd, dy_perm, a_rows=rt)
+    ffn()
+    ffn_ms_recompute = timed(ffn, 2)
+    del ffn
+    torch.cuda.empty_cache()
     if wr is not None:
         stages["route_backward"] = timed(lambda: B.moe_route_backward(x, wr, ids, w, gw, dx_perm=dxp, slot_row=sr), 2)
     flops = 12 * n * wl.d * wl.F
     tflops = flops / (ffn_ms / 1e3) / 1e12
+    tflops_recompute = flops / (ffn_ms_recompute / 1e3) / 1e12
     out = {
         "metric": BWD_METRIC, "value": round(wl.T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
-        "data": "synthetic (seeded random inputs, weights and output gradient of the page's layer shape; routing "
-                "and expert outputs from the forward's entry points)",
+        "data": "synthetic (seeded random inputs, weights and output gradient of the page's layer shape; routing, "
+                "expert outputs and gate/up pre-activations from the forward's entry points)",
         "config": {"workload": wl.name + "_backward", "tokens": wl.T, "hidden": wl.d, "experts": wl.E,
                    "top_k": wl.k, "expert_hidden": wl.F, "slots": n},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "grouped expert-FFN backward (7 GEMM launches, activation transposes; weights read in place)",
+                     "kernel": "grouped expert-FFN backward from the kept G | U (5 GEMM launches, activation "
+                               "transposes; weights read in place)",
                      "flops_per_launch": flops, "ms_per_launch": round(ffn_ms, 4),
-                     "note": "achieved counts 12 N d F; the G/U recompute (4 N d F) is extra work"},
+                     "note": "achieved counts 12 N d F (dH, dX, three weight gradients)"},
         "stages_ms": {k_: round(v, 4) for k_, v in stages.items()},
+        "recompute": {"ms_per_step": round(ms_recompute, 4), "tokens_per_s": round(wl.T / (ms_recompute / 1e3), 1),
+                      "grouped_ffn_backward_ms": round(ffn_ms_recompute, 4),
+                      "grouped_ffn_backward_tflops": round(tflops_recompute, 1),
+                      "mfma_frac": round(tflops_recompute / PEAK_BF16_TFLOPS, 4),
+                      "note": "G and U recomputed by a gate/up GEMM (4 N d F more work) instead of kept by the "
+                              "forward; achieved counts 12 N d F"},
     }
     if args.cpu_tokens > 0:
         from threadpoolctl import threadpool_info

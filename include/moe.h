@@ -143,12 +143,18 @@ moe_status moe_permute(int64_t T, int64_t d, int64_t E, int64_t k, moe_dtype dty
  *   y_perm   [n_max,d] dtype   out: y_perm[r] = W_d[e](silu(W_g[e] v_r) * (W_u[e] v_r)) for
  *                               input row v_r of expert e (first offsets[E] rows); may be
  *                               the same buffer as x_perm
+ *   gu_out [n_max,2F] dtype    NULL, or out: the gate and up pre-activations kept for
+ *                               the backward (moe_grouped_ffn_backward's gu): row r
+ *                               holds G = W_g[e] v_r in columns [0,F) and U = W_u[e] v_r
+ *                               in [F,2F), float32 sums rounded to dtype (first
+ *                               offsets[E] rows).  y_perm is the same with or without it.
+ *                               16-byte aligned.
  *   ws                          workspace: n_max*F*sizeof(dtype) bytes (the hidden activations h)
  */
 moe_status moe_grouped_ffn(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_dtype dtype,
                            const void* x_in, int64_t n_in, const int32_t* a_rows,
                            const int32_t* offsets, const void* w_gate, const void* w_up,
-                           const void* w_down, void* y_perm, void* ws, size_t* ws_bytes,
+                           const void* w_down, void* y_perm, void* gu_out, void* ws, size_t* ws_bytes,
                            void* stream);
 
 /*
@@ -182,13 +188,20 @@ moe_status moe_combine(int64_t T, int64_t d, int64_t k, moe_dtype dtype,
  *   share): topk_ids [T,k] and topk_w [T,k] are then required INPUTS, with
  *   negative ids for slots owned elsewhere; bias and logits_out must be NULL.
  *   offsets_out [E+1] int32, if not NULL, receives the expert row offsets.
- *   ws: query with ws == NULL (size grows with T*k*(2d+F)).
+ *   y_perm_out [T*k,d] dtype, if not NULL, receives the expert outputs in the
+ *   permutation's order (moe_layer_backward's y_perm) instead of the workspace.
+ *   gu_out [T*k,2F] dtype, if not NULL, receives the gate and up pre-activations
+ *   in the same row order (moe_grouped_ffn's gu_out; moe_layer_backward's gu).
+ *   Both 16-byte aligned; y is the same with or without them.
+ *   ws: query with ws == NULL (size grows with T*k*(2d+F); T*k*F without
+ *   y_perm_out).
  */
 moe_status moe_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t F, moe_dtype dtype,
                              const void* x, const void* w_router, const float* bias,
                              const void* w_gate, const void* w_up, const void* w_down,
                              void* y, float* logits_out, int32_t* topk_ids, float* topk_w,
-                             int32_t* offsets_out, void* ws, size_t* ws_bytes, void* stream);
+                             int32_t* offsets_out, void* y_perm_out, void* gu_out, void* ws,
+                             size_t* ws_bytes, void* stream);
 
 /*
  * moe_layer_forward_noalloc: moe_layer_forward without a workspace argument, for
@@ -208,7 +221,7 @@ moe_status moe_layer_forward_noalloc(int64_t T, int64_t d, int64_t E, int64_t k,
                                      const void* x, const void* w_router, const float* bias,
                                      const void* w_gate, const void* w_up, const void* w_down,
                                      void* y, float* logits_out, int32_t* topk_ids, float* topk_w,
-                                     int32_t* offsets_out, void* stream);
+                                     int32_t* offsets_out, void* y_perm_out, void* gu_out, void* stream);
 
 /*
  * moe_grouped_ffn_backward: gradients of the grouped SwiGLU FFN (the layer
@@ -218,10 +231,14 @@ moe_status moe_layer_forward_noalloc(int64_t T, int64_t d, int64_t E, int64_t k,
  *   dH = dY W_d, S = silu(X W_g^T), U = X W_u^T, H = S U,
  *   dU = dH S, dG = dH U silu'(X W_g^T),
  *   dX = dG W_g + dU W_u,  dW_d = dY^T H,  dW_g = dG^T X,  dW_u = dU^T X.
- * G and U are recomputed (nothing from the forward is needed but its inputs).
+ * G and U are recomputed from the inputs, or read from gu when the forward kept
+ * them (moe_grouped_ffn's gu_out): the backward then skips the gate/up product
+ * (a third of its matrix work) and holds no float32 dH.
  *   n_max, d, E, F, x_in, n_in, a_rows, offsets, w_gate, w_up, w_down: as in
  *                        moe_grouped_ffn
  *   dy_perm  [n_max,d] dtype   dY, rows grouped by expert (rows offsets[E].. unused)
+ *   gu     [n_max,2F] dtype   NULL (recompute G and U), or the forward's gu_out for
+ *                              the same rows, 16-byte aligned
  *   dx_perm  [n_max,d] dtype   out: dX (first offsets[E] rows written)
  *   dw_gate, dw_up [E,F,d] f32, dw_down [E,d,F] f32   out; zero for an expert with
  *                        no rows
@@ -230,14 +247,16 @@ moe_status moe_layer_forward_noalloc(int64_t T, int64_t d, int64_t E, int64_t k,
  *       (2 d + 3 F) (n_max + 63 E) dtype elements; float32 layers add transposed
  *       weight copies, 3 E d F elements; bf16 weights are read in place).
  * bf16: bf16 products, float32 accumulation; dG, dU and H are rounded to bf16
- * before the products that use them.  float32: float32 throughout.
+ * before the products that use them (with gu, G and U come in rounded to bf16
+ * as well).  float32: float32 throughout.  The workspace query depends on
+ * whether gu is NULL.
  * Errors as moe_grouped_ffn.
  */
 moe_status moe_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_dtype dtype,
                                     const void* x_in, int64_t n_in, const int32_t* a_rows,
                                     const int32_t* offsets, const void* w_gate, const void* w_up,
-                                    const void* w_down, const void* dy_perm, void* dx_perm,
-                                    float* dw_gate, float* dw_up, float* dw_down,
+                                    const void* w_down, const void* dy_perm, const void* gu,
+                                    void* dx_perm, float* dw_gate, float* dw_up, float* dw_down,
                                     void* ws, size_t* ws_bytes, void* stream);
 
 /*
@@ -315,6 +334,8 @@ moe_status moe_route_backward(int64_t T, int64_t d, int64_t E, int64_t k, moe_dt
  *   y_perm  [T*k,d] dtype  the forward's expert outputs, rows in the permutation's
  *                          order (experts ascending, tokens ascending within an
  *                          expert; moe_permute's order, recomputed here from topk_ids)
+ *   gu    [T*k,2F]  dtype  NULL, or the forward's gate/up pre-activations in the same
+ *                          row order (moe_layer_forward's gu_out): no recompute
  *   dy      [T,d]   dtype  output gradient
  *   dx      [T,d]   dtype  out: input gradient (experts, permutation and router)
  *   dw_router [E,d] f32    out (NULL when pre-routed); dbias [E] f32 out or NULL
@@ -329,8 +350,8 @@ moe_status moe_route_backward(int64_t T, int64_t d, int64_t E, int64_t k, moe_dt
 moe_status moe_layer_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t F, moe_dtype dtype,
                               const void* x, const void* w_router, const void* w_gate, const void* w_up,
                               const void* w_down, const int32_t* topk_ids, const float* topk_w,
-                              const void* y_perm, const void* dy, void* dx, float* dw_router, float* dbias,
-                              float* dw_gate, float* dw_up, float* dw_down, float* d_topk_w_out,
+                              const void* y_perm, const void* gu, const void* dy, void* dx, float* dw_router,
+                              float* dbias, float* dw_gate, float* dw_up, float* dw_down, float* d_topk_w_out,
                               void* ws, size_t* ws_bytes, void* stream);
 
 /*

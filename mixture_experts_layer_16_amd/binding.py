@@ -37,20 +37,20 @@ _f32 = ctypes.c_float
 _SIGS = {
     "moe_route": [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp],
     "moe_permute": [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp],
-    "moe_grouped_ffn": [_i64, _i64, _i64, _i64, _int, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp],
+    "moe_grouped_ffn": [_i64, _i64, _i64, _i64, _int, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp],
     "moe_combine": [_i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp],
     "moe_layer_forward": [_i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                          _vp, _vp, _szp, _vp],
+                          _vp, _vp, _vp, _vp, _szp, _vp],
     "moe_layer_forward_noalloc": [_i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                  _vp, _vp, _vp],
+                                  _vp, _vp, _vp, _vp, _vp],
     "moe_newton_schulz": [_i64, _i64, _i64, _int, _i64, _f32, _f32, _f32, _f32, _vp, _vp, _vp, _szp, _vp],
     "moe_grouped_ffn_backward": [_i64, _i64, _i64, _i64, _int, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                 _vp, _vp, _vp, _szp, _vp],
+                                 _vp, _vp, _vp, _vp, _szp, _vp],
     "moe_combine_backward": [_i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_route_backward": [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            _szp, _vp],
     "moe_layer_backward": [_i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp],
+                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _szp, _vp],
 }
 
 MUON_COEFFS = (3.4445, -4.7750, 2.0315)
@@ -141,10 +141,11 @@ def moe_permute(x, topk_ids, num_experts: int, copy_rows: bool = True):
     return offsets, row_token, slot_row, x_perm
 
 
-def moe_grouped_ffn(x_in, offsets, w_gate, w_up, w_down, y_perm=None, a_rows=None, n_max=None):
+def moe_grouped_ffn(x_in, offsets, w_gate, w_up, w_down, y_perm=None, a_rows=None, n_max=None, gu_out=None):
     """y_perm [n_max, d]: the SwiGLU FFN of each expert over its rows.  Without
     a_rows, x_in is x_perm (rows grouped by expert); with a_rows (row_token from
-    moe_permute), x_in is the token matrix x read in place."""
+    moe_permute), x_in is the token matrix x read in place.  gu_out [n_max, 2F]
+    (optional) receives the gate and up pre-activations for the backward."""
     d = x_in.shape[1]
     if a_rows is None:
         n_max, n_in = x_in.shape[0], 0
@@ -155,7 +156,7 @@ def moe_grouped_ffn(x_in, offsets, w_gate, w_up, w_down, y_perm=None, a_rows=Non
     if y_perm is None:
         y_perm = torch.empty(n_max, d, dtype=x_in.dtype, device=dev)
     head = (n_max, d, E, F, dtype_code(x_in.dtype), _p(x_in), n_in, _p(a_rows), _p(offsets), _p(w_gate), _p(w_up),
-            _p(w_down), _p(y_perm))
+            _p(w_down), _p(y_perm), _p(gu_out))
     ws = _ws(_query("moe_grouped_ffn", *head), dev)
     n = ctypes.c_size_t(ws.numel())
     _check("moe_grouped_ffn", lib().moe_grouped_ffn(*head, _p(ws), ctypes.byref(n), _stream(dev)))
@@ -174,21 +175,23 @@ def moe_combine(y_perm, slot_row, topk_w, out=None):
 
 class GroupedFfnBackward:
     """moe_grouped_ffn_backward with its outputs and workspace allocated once.
-    x_in is x_perm, or (a_rows given) the token matrix read through a_rows."""
+    x_in is x_perm, or (a_rows given) the token matrix read through a_rows; gu
+    the forward's gate/up pre-activations (moe_grouped_ffn's gu_out), or None to
+    recompute them."""
 
-    def __init__(self, x_in, offsets, w_gate, w_up, w_down, dy_perm, a_rows=None):
+    def __init__(self, x_in, offsets, w_gate, w_up, w_down, dy_perm, a_rows=None, gu=None):
         E, F, d = w_gate.shape
         n_max = dy_perm.shape[0]
         dev = dy_perm.device
         n_in = x_in.shape[0] if a_rows is not None else 0
-        self.t = (x_in, offsets, w_gate, w_up, w_down, dy_perm, a_rows)
+        self.t = (x_in, offsets, w_gate, w_up, w_down, dy_perm, a_rows, gu)
         self.dx = torch.empty(n_max, d, dtype=dy_perm.dtype, device=dev)
         self.dwg = torch.empty(E, F, d, dtype=torch.float32, device=dev)
         self.dwu = torch.empty(E, F, d, dtype=torch.float32, device=dev)
         self.dwd = torch.empty(E, d, F, dtype=torch.float32, device=dev)
         self.head = (n_max, d, E, F, dtype_code(dy_perm.dtype))
         self.mid = (_p(x_in), n_in, _p(a_rows), _p(offsets), _p(w_gate), _p(w_up), _p(w_down), _p(dy_perm),
-                    _p(self.dx), _p(self.dwg), _p(self.dwu), _p(self.dwd))
+                    _p(gu), _p(self.dx), _p(self.dwg), _p(self.dwu), _p(self.dwd))
         self.ws = _ws(_query("moe_grouped_ffn_backward", *self.head, *self.mid), dev)
 
     def __call__(self):
@@ -199,9 +202,9 @@ class GroupedFfnBackward:
         return self.dx, self.dwg, self.dwu, self.dwd
 
 
-def moe_grouped_ffn_backward(x_in, offsets, w_gate, w_up, w_down, dy_perm, a_rows=None):
+def moe_grouped_ffn_backward(x_in, offsets, w_gate, w_up, w_down, dy_perm, a_rows=None, gu=None):
     """(dx_perm, dW_gate, dW_up, dW_down) of the grouped SwiGLU FFN."""
-    return GroupedFfnBackward(x_in, offsets, w_gate, w_up, w_down, dy_perm, a_rows)()
+    return GroupedFfnBackward(x_in, offsets, w_gate, w_up, w_down, dy_perm, a_rows, gu)()
 
 
 def moe_combine_backward(dy, y_perm, slot_row, topk_w, dy_perm=None):
@@ -242,16 +245,18 @@ def moe_route_backward(x, w_router, topk_ids, topk_w, d_topk_w, dx_perm=None, sl
 class LayerBackward:
     """moe_layer_backward with its outputs and workspace allocated once.  The
     forward's routing (topk_ids, topk_w) and expert outputs y_perm (rows in the
-    permutation's order) are inputs; w_router None means pre-routed slots."""
+    permutation's order) are inputs; w_router None means pre-routed slots; gu the
+    forward's gate/up pre-activations (moe_layer_forward's want_gu), or None to
+    recompute them."""
 
     def __init__(self, x, w_router, w_gate, w_up, w_down, topk_ids, topk_w, y_perm, dy, want_bias: bool = True,
-                 want_d_topk_w: bool = False):
+                 want_d_topk_w: bool = False, gu=None):
         T, d = x.shape
         E, F, _ = w_gate.shape
         k = topk_ids.shape[1]
         dev = x.device
         routed = w_router is not None
-        self.t = (x, w_router, w_gate, w_up, w_down, topk_ids, topk_w, y_perm, dy)
+        self.t = (x, w_router, w_gate, w_up, w_down, topk_ids, topk_w, y_perm, gu, dy)
         self.dx = torch.empty(T, d, dtype=x.dtype, device=dev)
         self.dw_router = torch.empty(E, d, dtype=torch.float32, device=dev) if routed else None
         self.dbias = torch.empty(E, dtype=torch.float32, device=dev) if (routed and want_bias) else None
@@ -260,7 +265,7 @@ class LayerBackward:
         self.dw_down = torch.empty(E, d, F, dtype=torch.float32, device=dev)
         self.d_topk_w = torch.empty(T, k, dtype=torch.float32, device=dev) if want_d_topk_w else None
         self._head = (T, d, E, k, F, dtype_code(x.dtype), _p(x), _p(w_router), _p(w_gate), _p(w_up), _p(w_down),
-                      _p(topk_ids), _p(topk_w), _p(y_perm), _p(dy), _p(self.dx), _p(self.dw_router),
+                      _p(topk_ids), _p(topk_w), _p(y_perm), _p(gu), _p(dy), _p(self.dx), _p(self.dw_router),
                       _p(self.dbias), _p(self.dw_gate), _p(self.dw_up), _p(self.dw_down), _p(self.d_topk_w))
         self.ws = _ws(_query("moe_layer_backward", *self._head), dev)
         self._n = ctypes.c_size_t(self.ws.numel())
@@ -273,11 +278,11 @@ class LayerBackward:
 
 
 def moe_layer_backward(x, w_router, w_gate, w_up, w_down, topk_ids, topk_w, y_perm, dy, want_bias=True,
-                       want_d_topk_w=False):
+                       want_d_topk_w=False, gu=None):
     """One call of the whole layer backward; returns the LayerBackward object
     holding dx, dw_router, dbias, dw_gate, dw_up, dw_down and d_topk_w."""
     return LayerBackward(x, w_router, w_gate, w_up, w_down, topk_ids, topk_w, y_perm, dy, want_bias,
-                         want_d_topk_w)()
+                         want_d_topk_w, gu)()
 
 
 class NewtonSchulz:
@@ -311,7 +316,8 @@ class LayerForward:
     repeated calls (benchmarks, graph capture) allocate nothing."""
 
     def __init__(self, x, w_router, bias, w_gate, w_up, w_down, k: int, topk_ids=None, topk_w=None,
-                 want_logits: bool = False, want_routing: bool = False, want_offsets: bool = False):
+                 want_logits: bool = False, want_routing: bool = False, want_offsets: bool = False,
+                 want_y_perm: bool = False, want_gu: bool = False):
         self.x, self.w_router, self.bias = x, w_router, bias
         self.w_gate, self.w_up, self.w_down = w_gate, w_up, w_down
         T, d = x.shape
@@ -327,9 +333,12 @@ class LayerForward:
         else:
             self.topk_ids, self.topk_w = topk_ids, topk_w
         self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if want_offsets else None
+        # training: the expert outputs and gate/up pre-activations the backward takes
+        self.y_perm = torch.empty(T * k, d, dtype=x.dtype, device=dev) if want_y_perm else None
+        self.gu = torch.empty(T * k, 2 * F, dtype=x.dtype, device=dev) if want_gu else None
         self._head = (T, d, E, k, F, dtype_code(x.dtype), _p(x), _p(w_router), _p(bias), _p(w_gate), _p(w_up),
                       _p(w_down), _p(self.y), _p(self.logits), _p(self.topk_ids), _p(self.topk_w),
-                      _p(self.offsets))
+                      _p(self.offsets), _p(self.y_perm), _p(self.gu))
         self.ws = _ws(_query("moe_layer_forward", *self._head), dev)
         self._n = ctypes.c_size_t(self.ws.numel())
         self._ws_p = _p(self.ws)
@@ -341,10 +350,10 @@ class LayerForward:
 
 
 def moe_layer_forward(x, w_router, bias, w_gate, w_up, w_down, k: int, topk_ids=None, topk_w=None,
-                      want_logits=False, want_routing=False, want_offsets=False):
+                      want_logits=False, want_routing=False, want_offsets=False, want_y_perm=False, want_gu=False):
     """One call of the whole layer; returns the LayerForward object holding y
     and the optional outputs."""
     L = LayerForward(x, w_router, bias, w_gate, w_up, w_down, k, topk_ids, topk_w, want_logits, want_routing,
-                     want_offsets)
+                     want_offsets, want_y_perm, want_gu)
     L()
     return L

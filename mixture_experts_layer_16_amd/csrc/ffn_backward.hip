@@ -18,7 +18,9 @@
 //   * the I/O type is bf16 (MFMA bf16 products, float32 accumulation) or float32
 //     (float32 MFMA products throughout);
 //   * G and U are recomputed by the gate/up GEMM, whose epilogue turns them and
-//     dH into dG, dU (one [n, 2F] buffer) and H;
+//     dH into dG, dU (one [n, 2F] buffer) and H; or, when the forward kept them
+//     (G | U rounded to the I/O type), the dH GEMM's epilogue reads them and writes
+//     dG, dU and H itself (no recompute, no float32 dH);
 //   * the weight gradients contract over each expert's rows: the activations
 //     are transposed into a layout where expert e owns columns
 //     [poff[e], poff[e+1]) (its row count rounded up to 64, the gap zero-filled),
@@ -219,8 +221,8 @@ void gemm(GemmArgs a, int num_cu, hipStream_t s) {
 template <typename T, int BK>
 hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_in, int64_t n_in,
                           const int32_t* a_rows, const int32_t* raw_offsets, const void* w_gate, const void* w_up, const void* w_down,
-                          const void* dy_perm, void* dx_perm, float* dw_gate, float* dw_up, float* dw_down,
-                          const FfnBackwardScratch& w, int num_cu, hipStream_t s) {
+                          const void* dy_perm, const void* gu, void* dx_perm, float* dw_gate, float* dw_up,
+                          float* dw_down, const FfnBackwardScratch& w, int num_cu, hipStream_t s) {
   const int64_t np = w.n_pad;   // columns of the padded transposed layouts
   const T* Wg = static_cast<const T*>(w_gate);
   const T* Wu = static_cast<const T*>(w_up);
@@ -243,22 +245,35 @@ hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const 
     transpose_into(Wu, (int)F, (int)d, static_cast<T*>(w.wgu_t), 2 * F, (int)F, d * 2 * F);
   }
 
-  // dH = dY W_d (float32)
-  if constexpr (kBkn) {
-    GemmArgs a1 = args_grouped(dy_perm, nullptr, Wd, nullptr, d * F, offsets, (int)E, n_max, (int)F, (int)d, w.dh);
-    gemm<T, BK, EPI_F32, kFeatBKN>(a1, num_cu, s);
+  if (gu) {
+    // dH = dY W_d accumulated; the epilogue reads the saved G | U and writes dG | dU, H
+    const void* wd = kBkn ? static_cast<const void*>(Wd) : static_cast<const void*>(w.wd_t);
+    GemmArgs a1 = args_grouped(dy_perm, nullptr, wd, nullptr, d * F, offsets, (int)E, n_max, (int)F, (int)d, w.dgu);
+    a1.D = gu;
+    a1.C2 = w.h;
+    a1.ldc = 2 * F;
+    if constexpr (kBkn)
+      gemm<T, BK, EPI_DH_SWIGLU, kFeatBKN>(a1, num_cu, s);
+    else
+      gemm<T, BK, EPI_DH_SWIGLU>(a1, num_cu, s);
   } else {
-    GemmArgs a1 = args_grouped(dy_perm, nullptr, w.wd_t, nullptr, F * d, offsets, (int)E, n_max, (int)F, (int)d,
-                               w.dh);
-    gemm<T, BK, EPI_F32>(a1, num_cu, s);
+    // dH = dY W_d (float32)
+    if constexpr (kBkn) {
+      GemmArgs a1 = args_grouped(dy_perm, nullptr, Wd, nullptr, d * F, offsets, (int)E, n_max, (int)F, (int)d, w.dh);
+      gemm<T, BK, EPI_F32, kFeatBKN>(a1, num_cu, s);
+    } else {
+      GemmArgs a1 = args_grouped(dy_perm, nullptr, w.wd_t, nullptr, F * d, offsets, (int)E, n_max, (int)F, (int)d,
+                                 w.dh);
+      gemm<T, BK, EPI_F32>(a1, num_cu, s);
+    }
+    // recompute G, U; dG | dU and H
+    GemmArgs a2 = args_grouped(x_in, a_rows, w_gate, w_up, F * d, offsets, (int)E, n_max, (int)F, (int)d, w.dgu);
+    a2.a_rows_n = n_in;
+    a2.D = w.dh;
+    a2.C2 = w.h;
+    a2.ldc = 2 * F;
+    gemm<T, BK, EPI_SWIGLU_BWD>(a2, num_cu, s);
   }
-  // recompute G, U; dG | dU and H
-  GemmArgs a2 = args_grouped(x_in, a_rows, w_gate, w_up, F * d, offsets, (int)E, n_max, (int)F, (int)d, w.dgu);
-  a2.a_rows_n = n_in;
-  a2.D = w.dh;
-  a2.C2 = w.h;
-  a2.ldc = 2 * F;
-  gemm<T, BK, EPI_SWIGLU_BWD>(a2, num_cu, s);
   // dX = [dG | dU] [W_g ; W_u]: k < F reads W_g's rows, k >= F W_u's
   if constexpr (kBkn) {
     GemmArgs a3 = args_grouped(w.dgu, nullptr, Wg, Wu, F * d, offsets, (int)E, n_max, (int)d, (int)(2 * F), dx_perm);
@@ -314,12 +329,12 @@ hipError_t ffn_backward_t(int64_t n_max, int64_t d, int64_t E, int64_t F, const 
 hipError_t launch_grouped_ffn_backward(int dtype, int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_in,
                                        int64_t n_in, const int32_t* a_rows, const int32_t* offsets,
                                        const void* w_gate, const void* w_up, const void* w_down, const void* dy_perm,
-                                       void* dx_perm, float* dw_gate, float* dw_up, float* dw_down,
+                                       const void* gu, void* dx_perm, float* dw_gate, float* dw_up, float* dw_down,
                                        const FfnBackwardScratch& w, int num_cu, hipStream_t s) {
   if (dtype == 1)
-    return ffn_backward_t<bf16, 64>(n_max, d, E, F, x_in, n_in, a_rows, offsets, w_gate, w_up, w_down, dy_perm,
+    return ffn_backward_t<bf16, 64>(n_max, d, E, F, x_in, n_in, a_rows, offsets, w_gate, w_up, w_down, dy_perm, gu,
                                     dx_perm, dw_gate, dw_up, dw_down, w, num_cu, s);
-  return ffn_backward_t<float, 32>(n_max, d, E, F, x_in, n_in, a_rows, offsets, w_gate, w_up, w_down, dy_perm,
+  return ffn_backward_t<float, 32>(n_max, d, E, F, x_in, n_in, a_rows, offsets, w_gate, w_up, w_down, dy_perm, gu,
                                    dx_perm, dw_gate, dw_up, dw_down, w, num_cu, s);
 }
 

@@ -30,12 +30,23 @@ namespace moe {
 
 enum GemmFeature { kFeatGroups = 1, kFeatStrides = 2, kFeatBKN = 4 };
 
-enum Epilogue { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_F32_BIAS = 2, EPI_AXPBY = 3, EPI_SWIGLU_BWD = 4, EPI_F32 = 5 };
+enum Epilogue {
+  EPI_STORE = 0,
+  EPI_SWIGLU = 1,
+  EPI_F32_BIAS = 2,
+  EPI_AXPBY = 3,
+  EPI_SWIGLU_BWD = 4,
+  EPI_F32 = 5,
+  EPI_SWIGLU_SAVE = 6,   // EPI_SWIGLU that also stores G | U (rounded to T) for the backward
+  EPI_DH_SWIGLU = 7      // accumulators are dH; G | U read back: dG | dU and H, as EPI_SWIGLU_BWD
+};
 // float32 output: the accumulators plus an optional per-column bias (EPI_F32_BIAS),
 // or as they are (EPI_F32)
 constexpr bool f32_epilogue(int epi) { return epi == EPI_F32_BIAS || epi == EPI_F32; }
 // Epilogues whose B tile holds gate rows and the matching up rows.
-constexpr bool paired_epilogue(int epi) { return epi == EPI_SWIGLU || epi == EPI_SWIGLU_BWD; }
+constexpr bool paired_epilogue(int epi) { return epi == EPI_SWIGLU || epi == EPI_SWIGLU_BWD || epi == EPI_SWIGLU_SAVE; }
+// Epilogues that store dG | dU (C, row stride ldc) and H (C2) from G, U and dH.
+constexpr bool swiglu_grad_epilogue(int epi) { return epi == EPI_SWIGLU_BWD || epi == EPI_DH_SWIGLU; }
 
 // f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
 template <int N, int I = 0, typename F> __device__ __forceinline__ void static_for(F&& f) {
@@ -82,12 +93,15 @@ struct GemmArgs {
   float alpha, beta;      // EPI_AXPBY: C = alpha * (A B^T) + beta * D
   const void* D;          // EPI_AXPBY: [rows, N], same layout and type as C
                           // EPI_SWIGLU_BWD: dH [rows, N] float32
+                          // EPI_DH_SWIGLU: G | U [rows, 2N], type T (G in columns
+                          // [0, N), U in [N, 2N))
   int64_t lda, ldb;       // row strides of A and B in elements (0: K)
   const int32_t* kseg;    // [G+1] device k offsets (multiples of BK): group g contracts
                           // over k in [kseg[g], kseg[g+1]) (nullptr: [0, K) for all)
   int32_t a_shared;       // 1: every group reads the same A rows (row r of a group's
                           // tile block is A row r, not the group's first row + r)
-  void* C2;               // EPI_SWIGLU_BWD: H = silu(G) * U, [rows, N]
+  void* C2;               // EPI_SWIGLU_BWD, EPI_DH_SWIGLU: H = silu(G) * U, [rows, N]
+                          // EPI_SWIGLU_SAVE: G | U [rows, 2N] (G in columns [0, N))
   int64_t ldc;            // row stride of C in elements (0: N)
   int64_t ksa, ksb;       // elements from one BK-deep k-slice of A (B) to the next
                           // (0: BK).  With lda = BK and ksa = rows * BK, A is stored
@@ -689,9 +703,22 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
     };
     // (EPI_SWIGLU_BWD's three outputs stay on the direct path: staging them costs
     // the K loop registers)
-    constexpr bool kStaged = EPI != EPI_AXPBY && EPI != EPI_SWIGLU_BWD && NT == 512 && Cfg::WTM == 64 &&
+    constexpr bool kStaged = EPI != EPI_AXPBY && !swiglu_grad_epilogue(EPI) && NT == 512 && Cfg::WTM == 64 &&
                              8 * kEpiWaveBytes <= Cfg::kStageBytes;
-    if constexpr (kStaged) {
+    if constexpr (kStaged && EPI == EPI_SWIGLU_SAVE) {
+      // h = silu(G) U, then G and U themselves into the two halves of C2's rows
+      staged(
+          TypeTag<T>{},
+          [&](int mi, int ni, int q, int i) {
+            const float gv = acc[mi][ni][4 * q + i];
+            return gv / (1.0f + __expf(-gv)) * acc[mi][ni + NI / 2][4 * q + i];
+          },
+          p.C, (int64_t)p.N);
+      staged(TypeTag<T>{}, [&](int mi, int ni, int q, int i) { return acc[mi][ni][4 * q + i]; }, p.C2,
+             2 * (int64_t)p.N);
+      staged(TypeTag<T>{}, [&](int mi, int ni, int q, int i) { return acc[mi][ni + NI / 2][4 * q + i]; },
+             static_cast<T*>(p.C2) + p.N, 2 * (int64_t)p.N);
+    } else if constexpr (kStaged) {
       typedef typename std::conditional<f32_epilogue(EPI), float, T>::type OT;
       staged(
           TypeTag<OT>{},
@@ -707,12 +734,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
             }
           },
           p.C, (int64_t)p.N);
-    } else if constexpr (f32_epilogue(EPI)) {
-      static_assert(!f32_epilogue(EPI), "float32 outputs take the staged epilogue");
+    } else if constexpr (f32_epilogue(EPI) || EPI == EPI_SWIGLU_SAVE) {
+      static_assert(!f32_epilogue(EPI) && EPI != EPI_SWIGLU_SAVE, "this epilogue takes the staged path");
     } else {
       constexpr int NO = paired_epilogue(EPI) ? NI / 2 : NI;
       constexpr int CW = paired_epilogue(EPI) ? Cfg::WTN / 2 : Cfg::WTN;
-      const int64_t ldc = (EPI == EPI_SWIGLU_BWD && p.ldc) ? p.ldc : p.N;
+      const int64_t ldc = (swiglu_grad_epilogue(EPI) && p.ldc) ? p.ldc : p.N;
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         const int r = (wm + WM * mi) * 32 + (lane & 31);
@@ -752,17 +779,38 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
 #pragma unroll
             for (int qq = 0; qq < 2; ++qq) {
               const int col = en0 + wn * CW + ni * 32 + 8 * (q + qq) + h4;
-              if constexpr (EPI == EPI_SWIGLU_BWD) {
-                // recomputed G and U with the incoming dH:  S = silu(G), H = S U,
-                // dU = dH S, dG = dH U silu'(G); dG and dU go to the row's two halves
-                f32x4 dh = {0.f, 0.f, 0.f, 0.f};
-                if (col < p.N)
-                  dh = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.D) + (em0 + r) * (int64_t)p.N +
-                                                       col);
+              if constexpr (swiglu_grad_epilogue(EPI)) {
+                // S = silu(G), H = S U, dU = dH S, dG = dH U silu'(G); dG and dU go to
+                // the row's two halves.  EPI_SWIGLU_BWD: G, U recomputed (accumulators),
+                // dH read; EPI_DH_SWIGLU: dH accumulated, G, U read (saved by the forward)
+                float gg[4], uu[4], dh[4];
+                if constexpr (EPI == EPI_SWIGLU_BWD) {
+                  f32x4 dv4 = {0.f, 0.f, 0.f, 0.f};
+                  if (col < p.N)
+                    dv4 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.D) +
+                                                          (em0 + r) * (int64_t)p.N + col);
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) {
+                    gg[i] = acc[mi][ni][4 * (q + qq) + i];
+                    uu[i] = acc[mi][ni + NI / 2][4 * (q + qq) + i];
+                    dh[i] = dv4[i];
+                  }
+                } else {
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) {
+                    gg[i] = 0.f;
+                    uu[i] = 0.f;
+                    dh[i] = acc[mi][ni][4 * (q + qq) + i];
+                  }
+                  if (col < p.N) {
+                    const T* gu = static_cast<const T*>(p.D) + (em0 + r) * 2 * (int64_t)p.N + col;
+                    load4(gu, gg);
+                    load4(gu + p.N, uu);
+                  }
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                  const float g = acc[mi][ni][4 * (q + qq) + i];
-                  const float u = acc[mi][ni + NI / 2][4 * (q + qq) + i];
+                  const float g = gg[i], u = uu[i];
                   const float sg = 1.0f / (1.0f + __expf(-g));
                   const float sv = g * sg;
                   v[qq][0][i] = dh[i] * u * (sg * (1.0f + g * (1.0f - sg)));
@@ -787,7 +835,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void grouped_gemm_kernel(GemmArgs 
                 }
               }
             }
-            constexpr int NOUT_ = EPI == EPI_SWIGLU_BWD ? 3 : 1;
+            constexpr int NOUT_ = swiglu_grad_epilogue(EPI) ? 3 : 1;
             if constexpr (sizeof(T) == 2) {
               const int colp = en0 + wn * CW + ni * 32 + 8 * (q + (lane >> 5));   // this lane's 8 columns
 #pragma unroll

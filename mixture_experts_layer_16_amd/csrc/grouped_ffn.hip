@@ -40,7 +40,7 @@ constexpr int kDownColumnGroup = 2;
 template <typename T, int BK, int STAGES, int WM, int WN, int PD>
 void run(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm, int64_t n_in, const int32_t* a_rows,
          const int32_t* offsets,
-         const void* w_gate, const void* w_up, const void* w_down, void* y_perm, void* h, int num_cu,
+         const void* w_gate, const void* w_up, const void* w_down, void* y_perm, void* h, void* gu_out, int num_cu,
          hipStream_t stream) {
   GemmArgs gu{};
   gu.A = x_perm;
@@ -58,9 +58,15 @@ void run(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm, int
   gu.bias = nullptr;
   gu.n_group = kGateUpColumnGroup;
   gu.m_chunk = kGateUpRowChunk;
-  hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, WM, WN, STAGES, EPI_SWIGLU, PD>), dim3(num_cu),
-                     dim3(WM * WN * 64), 0,
-                     stream, gu);
+  if (gu_out) {
+    // G | U kept for the backward (rows of [n_max, 2F], G in the first F columns)
+    gu.C2 = gu_out;
+    hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, WM, WN, STAGES, EPI_SWIGLU_SAVE, PD>), dim3(num_cu),
+                       dim3(WM * WN * 64), 0, stream, gu);
+  } else {
+    hipLaunchKernelGGL((grouped_gemm_kernel<T, 256, 256, BK, WM, WN, STAGES, EPI_SWIGLU, PD>), dim3(num_cu),
+                       dim3(WM * WN * 64), 0, stream, gu);
+  }
 
   GemmArgs dn{};
   dn.A = h;
@@ -86,14 +92,14 @@ void run(int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm, int
 
 hipError_t launch_grouped_ffn(int dtype, int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_perm,
                               int64_t n_in, const int32_t* a_rows, const int32_t* offsets, const void* w_gate,
-                              const void* w_up, const void* w_down, void* y_perm, void* h, int num_cu,
-                              hipStream_t stream) {
+                              const void* w_up, const void* w_down, void* y_perm, void* h, void* gu_out,
+                              int num_cu, hipStream_t stream) {
   if (dtype == 1)
-    run<bf16, 64, 2, 4, 2, 1>(n_max, d, E, F, x_perm, n_in, a_rows, offsets, w_gate, w_up, w_down, y_perm, h, num_cu,
-                              stream);
+    run<bf16, 64, 2, 4, 2, 1>(n_max, d, E, F, x_perm, n_in, a_rows, offsets, w_gate, w_up, w_down, y_perm, h,
+                              gu_out, num_cu, stream);
   else
     run<float, 32, 2, 4, 2, 1>(n_max, d, E, F, x_perm, n_in, a_rows, offsets, w_gate, w_up, w_down, y_perm, h,
-                               num_cu, stream);
+                               gu_out, num_cu, stream);
   return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ hipError_t launch_grouped_ffn(int dtype, int64_t n_max, int64_t d, int64_t E, in
                               const void* x_perm, int64_t n_in, const int32_t* a_rows, const int32_t* offsets,
                               const void* w_gate,
                               const void* w_up, const void* w_down, void* y_perm, void* h,
-                              int num_cu, hipStream_t stream);
+                              void* gu_out, int num_cu, hipStream_t stream);
 
 // Muon's Newton-Schulz orthogonalisation of n bf16 matrices [R, C] (R, C multiples
 // of 64): g in, x out; xw0 and xw1 [n, R', C'], A and B [n, R', R']
@@ -51,7 +51,7 @@ struct FfnBackwardScratch {
   int32_t* pblk_expert;  // [n_pad / 64] expert of each 64-wide padded column block
   void* wd_t;      // [E, F, d]   W_d transposed (float32 layers only)
   void* wgu_t;     // [E, d, 2F]  W_g and W_u transposed, side by side (float32 layers only)
-  float* dh;       // [n_max, F]  dH (float32)
+  float* dh;       // [n_max, F]  dH (float32); nullptr when the forward kept G | U
   void* dgu;       // [n_max, 2F] dG | dU (I/O)
   void* h;         // [n_max, F]  H recomputed (I/O)
   void* x_t;       // [d, n_pad]  expert rows of the input, transposed and padded, stored
@@ -64,9 +64,9 @@ struct FfnBackwardScratch {
 };
 hipError_t launch_grouped_ffn_backward(int dtype, int64_t n_max, int64_t d, int64_t E, int64_t F, const void* x_in,
                                        int64_t n_in, const int32_t* a_rows, const int32_t* offsets, const void* w_gate,
-                                       const void* w_up, const void* w_down, const void* dy_perm, void* dx_perm,
-                                       float* dw_gate, float* dw_up, float* dw_down, const FfnBackwardScratch& w,
-                                       int num_cu, hipStream_t stream);
+                                       const void* w_up, const void* w_down, const void* dy_perm, const void* gu,
+                                       void* dx_perm, float* dw_gate, float* dw_up, float* dw_down,
+                                       const FfnBackwardScratch& w, int num_cu, hipStream_t stream);
 
 // Weighted un-permute: y[t] = sum_j w[t,j] * y_perm[slot_row[t,j]].
 hipError_t launch_combine(int dtype, int64_t T, int64_t d, int64_t k, const void* y_perm,

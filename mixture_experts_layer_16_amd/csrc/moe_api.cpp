@@ -107,9 +107,10 @@ struct Carver {
   }
 };
 
-// Scratch of the grouped-FFN backward for n_max rows (element size es).
+// Scratch of the grouped-FFN backward for n_max rows (element size es); saved: the
+// forward's G | U are given (no float32 dH buffer).
 void carve_ffn_backward(Carver& c, moe::FfnBackwardScratch& w, int64_t n_max, int64_t d, int64_t E, int64_t F,
-                        size_t es) {
+                        size_t es, bool saved) {
   const int64_t n_pad = (n_max + 63 * E + 63) / 64 * 64;
   w.soff = static_cast<int32_t*>(c.take((size_t)(E + 1) * 4));
   w.poff = static_cast<int32_t*>(c.take((size_t)(E + 1) * 4));
@@ -117,7 +118,7 @@ void carve_ffn_backward(Carver& c, moe::FfnBackwardScratch& w, int64_t n_max, in
   // transposed weight copies: float32 only (16-bit weights are read in place)
   w.wd_t = es == 4 ? c.take((size_t)E * F * d * es) : nullptr;
   w.wgu_t = es == 4 ? c.take((size_t)E * d * 2 * F * es) : nullptr;
-  w.dh = static_cast<float*>(c.take((size_t)n_max * F * 4));
+  w.dh = saved ? nullptr : static_cast<float*>(c.take((size_t)n_max * F * 4));
   w.dgu = c.take((size_t)n_max * 2 * F * es);
   w.h = c.take((size_t)n_max * F * es);
   w.x_t = c.take((size_t)d * n_pad * es);
@@ -192,8 +193,8 @@ moe_status moe_permute(int64_t T, int64_t d, int64_t E, int64_t k, moe_dtype dty
 
 moe_status moe_grouped_ffn(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_dtype dtype, const void* x_in,
                            int64_t n_in, const int32_t* a_rows, const int32_t* offsets, const void* w_gate,
-                           const void* w_up, const void* w_down, void* y_perm, void* ws, size_t* ws_bytes,
-                           void* stream) {
+                           const void* w_up, const void* w_down, void* y_perm, void* gu_out, void* ws,
+                           size_t* ws_bytes, void* stream) {
   moe_status st = check_ffn_dims(n_max, d, E, F);
   if (st != MOE_OK) return st;
   if ((st = check_dtype(dtype)) != MOE_OK) return st;
@@ -207,20 +208,21 @@ moe_status moe_grouped_ffn(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_d
     return MOE_OK;
   }
   if (!ok16(x_in) || !opt4(a_rows) || !ok4(offsets) || !ok16(w_gate) || !ok16(w_up) || !ok16(w_down) ||
-      !ok16(y_perm))
+      !ok16(y_perm) || !opt16(gu_out))
     return MOE_ERR_INVALID_ARG;
   if (workspace_step(ws, ws_bytes, need, &st)) return st;
   int ncu = 0;
   if ((st = num_cu(&ncu)) != MOE_OK) return st;
   return hip_status(moe::launch_grouped_ffn(dtype, n_max, d, E, F, x_in, a_rows ? n_in : n_max, a_rows, offsets,
-                                            w_gate, w_up, w_down, y_perm, ws, ncu, static_cast<hipStream_t>(stream)));
+                                            w_gate, w_up, w_down, y_perm, ws, gu_out, ncu,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int64_t F, moe_dtype dtype,
                                     const void* x_in, int64_t n_in, const int32_t* a_rows, const int32_t* offsets,
                                     const void* w_gate, const void* w_up, const void* w_down, const void* dy_perm,
-                                    void* dx_perm, float* dw_gate, float* dw_up, float* dw_down, void* ws,
-                                    size_t* ws_bytes, void* stream) {
+                                    const void* gu, void* dx_perm, float* dw_gate, float* dw_up, float* dw_down,
+                                    void* ws, size_t* ws_bytes, void* stream) {
   moe_status st = check_ffn_dims(n_max, d, E, F);
   if (st != MOE_OK) return st;
   if ((st = check_dtype(dtype)) != MOE_OK) return st;
@@ -232,23 +234,23 @@ moe_status moe_grouped_ffn_backward(int64_t n_max, int64_t d, int64_t E, int64_t
   if (!ffn_backward_fits(n_max, E)) return MOE_ERR_UNSUPPORTED;
   moe::FfnBackwardScratch w{};
   Carver c0(nullptr);
-  carve_ffn_backward(c0, w, n_max, d, E, F, es);
+  carve_ffn_backward(c0, w, n_max, d, E, F, es, gu != nullptr);
   const size_t need = c0.used;
   if (ws == nullptr && ws_bytes != nullptr) {
     *ws_bytes = need;
     return MOE_OK;
   }
   if (!ok16(x_in) || !opt4(a_rows) || !ok4(offsets) || !ok16(w_gate) || !ok16(w_up) || !ok16(w_down) ||
-      !ok16(dy_perm) || !ok16(dx_perm) || !ok16(dw_gate) || !ok16(dw_up) || !ok16(dw_down))
+      !ok16(dy_perm) || !opt16(gu) || !ok16(dx_perm) || !ok16(dw_gate) || !ok16(dw_up) || !ok16(dw_down))
     return MOE_ERR_INVALID_ARG;
   if (workspace_step(ws, ws_bytes, need, &st)) return st;
   int ncu = 0;
   if ((st = num_cu(&ncu)) != MOE_OK) return st;
   Carver cv(ws);
-  carve_ffn_backward(cv, w, n_max, d, E, F, es);
+  carve_ffn_backward(cv, w, n_max, d, E, F, es, gu != nullptr);
   return hip_status(moe::launch_grouped_ffn_backward(dtype, n_max, d, E, F, x_in, a_rows ? n_in : n_max, a_rows,
-                                                     offsets, w_gate, w_up, w_down, dy_perm, dx_perm, dw_gate, dw_up,
-                                                     dw_down, w, ncu, static_cast<hipStream_t>(stream)));
+                                                     offsets, w_gate, w_up, w_down, dy_perm, gu, dx_perm, dw_gate,
+                                                     dw_up, dw_down, w, ncu, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_combine_backward(int64_t T, int64_t d, int64_t k, moe_dtype dtype, const void* dy,
@@ -298,8 +300,9 @@ moe_status moe_route_backward(int64_t T, int64_t d, int64_t E, int64_t k, moe_dt
 moe_status moe_layer_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t F, moe_dtype dtype,
                               const void* x, const void* w_router, const void* w_gate, const void* w_up,
                               const void* w_down, const int32_t* topk_ids, const float* topk_w, const void* y_perm,
-                              const void* dy, void* dx, float* dw_router, float* dbias, float* dw_gate, float* dw_up,
-                              float* dw_down, float* d_topk_w_out, void* ws, size_t* ws_bytes, void* stream) {
+                              const void* gu, const void* dy, void* dx, float* dw_router, float* dbias, float* dw_gate,
+                              float* dw_up, float* dw_down, float* d_topk_w_out, void* ws, size_t* ws_bytes,
+                              void* stream) {
   moe_status st = check_tdek(T, d, E, k);
   if (st != MOE_OK) return st;
   if (F <= 0) return MOE_ERR_INVALID_ARG;
@@ -325,7 +328,7 @@ moe_status moe_layer_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_
     dy_perm = c.take((size_t)slots * d * es);
     dx_perm = c.take((size_t)slots * d * es);
     x_perm = in_place ? nullptr : c.take((size_t)slots * d * es);
-    carve_ffn_backward(c, fw, slots, d, E, F, es);
+    carve_ffn_backward(c, fw, slots, d, E, F, es, gu != nullptr);
     if (routed) carve_route_backward(c, rw, T, d, E, es, nullptr);
   };
   int32_t *offsets, *row_token, *slot_row, *counts;
@@ -339,8 +342,8 @@ moe_status moe_layer_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_
     return MOE_OK;
   }
   if (!ok16(x) || !ok16(w_gate) || !ok16(w_up) || !ok16(w_down) || !ok4(topk_ids) || !ok4(topk_w) ||
-      !ok16(y_perm) || !ok16(dy) || !ok16(dx) || !ok16(dw_gate) || !ok16(dw_up) || !ok16(dw_down) ||
-      !opt4(d_topk_w_out))
+      !ok16(y_perm) || !opt16(gu) || !ok16(dy) || !ok16(dx) || !ok16(dw_gate) || !ok16(dw_up) ||
+      !ok16(dw_down) || !opt4(d_topk_w_out))
     return MOE_ERR_INVALID_ARG;
   if (routed) {
     if (!ok16(w_router) || !ok16(dw_router) || !opt4(dbias)) return MOE_ERR_INVALID_ARG;
@@ -361,9 +364,9 @@ moe_status moe_layer_backward(int64_t T, int64_t d, int64_t E, int64_t k, int64_
       MOE_OK)
     return st;
   if ((st = hip_status(moe::launch_grouped_ffn_backward(dtype, slots, d, E, F, in_place ? x : x_perm,
-                                                        in_place ? T : slots, in_place ? row_token : nullptr, offsets, w_gate, w_up,
-                                                        w_down, dy_perm, dx_perm, dw_gate, dw_up, dw_down, fw, ncu,
-                                                        s))) != MOE_OK)
+                                                        in_place ? T : slots, in_place ? row_token : nullptr,
+                                                        offsets, w_gate, w_up, w_down, dy_perm, gu, dx_perm, dw_gate,
+                                                        dw_up, dw_down, fw, ncu, s))) != MOE_OK)
     return st;
   if (routed)
     return hip_status(moe::launch_route_backward(dtype, T, d, E, k, x, w_router, topk_ids, topk_w, g, dx_perm,
@@ -418,7 +421,8 @@ moe_status moe_combine(int64_t T, int64_t d, int64_t k, moe_dtype dtype, const v
 moe_status moe_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t F, moe_dtype dtype, const void* x,
                              const void* w_router, const float* bias, const void* w_gate, const void* w_up,
                              const void* w_down, void* y, float* logits_out, int32_t* topk_ids, float* topk_w,
-                             int32_t* offsets_out, void* ws, size_t* ws_bytes, void* stream) {
+                             int32_t* offsets_out, void* y_perm_out, void* gu_out, void* ws, size_t* ws_bytes,
+                             void* stream) {
   moe_status st = check_tdek(T, d, E, k);
   if (st != MOE_OK) return st;
   if (F <= 0) return MOE_ERR_INVALID_ARG;
@@ -437,7 +441,8 @@ moe_status moe_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
   int32_t* row_token = static_cast<int32_t*>(c.take(slots * 4));
   int32_t* slot_row = static_cast<int32_t*>(c.take(slots * 4));
   int32_t* counts = static_cast<int32_t*>(c.take(permute_ws(T, E)));
-  void* y_perm = c.take(slots * (size_t)d * es);   // also holds x_perm when x is not read in place
+  // also holds x_perm when x is not read in place
+  void* y_perm = y_perm_out ? y_perm_out : c.take(slots * (size_t)d * es);
   void* h = c.take(slots * (size_t)F * es);
   const size_t need = c.used;
 
@@ -446,7 +451,7 @@ moe_status moe_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
     return MOE_OK;
   }
   if (!ok16(x) || !ok16(w_gate) || !ok16(w_up) || !ok16(w_down) || !ok16(y) || !opt16(logits_out) ||
-      !opt4(offsets_out))
+      !opt4(offsets_out) || !opt16(y_perm_out) || !opt16(gu_out))
     return MOE_ERR_INVALID_ARG;
   if (routed) {
     if (!ok16(w_router) || !opt4(bias) || !opt4(topk_ids) || !opt4(topk_w)) return MOE_ERR_INVALID_ARG;
@@ -473,7 +478,7 @@ moe_status moe_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
     return st;
   if ((st = hip_status(moe::launch_grouped_ffn(dtype, (int64_t)slots, d, E, F, in_place ? x : y_perm,
                                                in_place ? T : (int64_t)slots, in_place ? row_token : nullptr, offsets, w_gate, w_up, w_down,
-                                               y_perm, h, ncu, s))) != MOE_OK)
+                                               y_perm, h, gu_out, ncu, s))) != MOE_OK)
     return st;
   return hip_status(moe::launch_combine(dtype, T, d, k, y_perm, slot_row, w, y, s));
 }

@@ -48,16 +48,17 @@ extern "C" moe_status moe_layer_forward_noalloc(int64_t T, int64_t d, int64_t E,
                                                 moe_dtype dtype, const void* x, const void* w_router,
                                                 const float* bias, const void* w_gate, const void* w_up,
                                                 const void* w_down, void* y, float* logits_out, int32_t* topk_ids,
-                                                float* topk_w, int32_t* offsets_out, void* stream) {
+                                                float* topk_w, int32_t* offsets_out, void* y_perm_out, void* gu_out,
+                                                void* stream) {
   // the workspace this call needs (sizes are checked; nothing is launched)
   size_t need = 0;
   moe_status st = moe_layer_forward(T, d, E, k, F, dtype, x, w_router, bias, w_gate, w_up, w_down, y, logits_out,
-                                    topk_ids, topk_w, offsets_out, nullptr, &need, stream);
+                                    topk_ids, topk_w, offsets_out, y_perm_out, gu_out, nullptr, &need, stream);
   if (st != MOE_OK) return st;
   if (need > kScratchBytes) return MOE_ERR_WORKSPACE;
   void* ws = nullptr;
   if ((st = scratch_on_current_device(&ws)) != MOE_OK) return st;
   size_t have = kScratchBytes;
   return moe_layer_forward(T, d, E, k, F, dtype, x, w_router, bias, w_gate, w_up, w_down, y, logits_out, topk_ids,
-                           topk_w, offsets_out, ws, &have, stream);
+                           topk_w, offsets_out, y_perm_out, gu_out, ws, &have, stream);
 }

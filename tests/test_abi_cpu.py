@@ -56,36 +56,42 @@ def test_permute_workspace_query():
 
 
 def test_grouped_ffn_workspace_query():
-    st, n = q("moe_grouped_ffn", 5000, 256, 12, 192, 1, None, 0, *([None] * 6))
+    st, n = q("moe_grouped_ffn", 5000, 256, 12, 192, 1, None, 0, *([None] * 7))
     assert st == OK and n == ru(5000 * 192 * 2)
-    st, n = q("moe_grouped_ffn", 5000, 256, 12, 192, 0, None, 0, *([None] * 6))
+    st, n = q("moe_grouped_ffn", 5000, 256, 12, 192, 0, None, 0, *([None] * 7))
     assert st == OK and n == ru(5000 * 192 * 4)
+    st, n = q("moe_grouped_ffn", 5000, 256, 12, 192, 1, None, 0, *([None] * 6), P)
+    assert st == OK and n == ru(5000 * 192 * 2)     # G | U go to the caller's buffer
 
 
-def layer_ws(T, d, E, k, F, es, routed=True):
+def layer_ws(T, d, E, k, F, es, routed=True, y_perm_out=False):
     s = T * k
     n = 0
     if routed:
         n += ru(T * E * 4) + ru(s * 4) + ru(s * 4)     # logits, ids, weights
     n += ru((E + 1) * 4) + ru(s * 4) + ru(s * 4)         # offsets, row_token, slot_row
     n += ru(((T + 255) // 256) * E * 4)                  # block counts
-    n += ru(s * d * es) + ru(s * F * es)                  # x_perm (reused as y_perm), h
+    n += 0 if y_perm_out else ru(s * d * es)              # x_perm (reused as y_perm)
+    n += ru(s * F * es)                                   # h
     return n
 
 
 @pytest.mark.parametrize("T,d,E,k,F,dt", [(256, 128, 16, 2, 64, 0), (65536, 6144, 384, 8, 1792, 1),
                                           (777, 192, 11, 3, 192, 1)])
 def test_layer_workspace_query(T, d, E, k, F, dt):
-    st, n = q("moe_layer_forward", T, d, E, k, F, dt, *([None] * 11))
+    st, n = q("moe_layer_forward", T, d, E, k, F, dt, *([None] * 13))
     assert st == OK
     assert n == layer_ws(T, d, E, k, F, 2 if dt == 1 else 4, routed=False)   # w_router NULL: pre-routed
-    st, n = q("moe_layer_forward", T, d, E, k, F, dt, None, P, *([None] * 9))
+    st, n = q("moe_layer_forward", T, d, E, k, F, dt, None, P, *([None] * 11))
     assert st == OK and n == layer_ws(T, d, E, k, F, 2 if dt == 1 else 4, routed=True)
+    # y_perm (and x_perm) in the caller's buffer; G | U never take workspace
+    st, n = q("moe_layer_forward", T, d, E, k, F, dt, None, P, *([None] * 9), P, P)
+    assert st == OK and n == layer_ws(T, d, E, k, F, 2 if dt == 1 else 4, routed=True, y_perm_out=True)
 
 
 def test_page_shape_workspace_fits_and_reuses_x_perm():
     # 65,536 tokens at the page's shape: x_perm 6.44 GB + h 1.88 GB, y_perm shares x_perm
-    st, n = q("moe_layer_forward", 65536, 6144, 384, 8, 1792, 1, None, P, *([None] * 9))
+    st, n = q("moe_layer_forward", 65536, 6144, 384, 8, 1792, 1, None, P, *([None] * 11))
     assert st == OK and 8.2e9 < n < 8.5e9
 
 
@@ -117,18 +123,19 @@ def test_route_without_workspace_when_one_is_needed():
     assert st == WORKSPACE
 
 
-def ffn(n_max=1000, d=128, E=4, F=128, dt=1, xp=P, n_in=0, rows=None, off=P, wg=P, wu=P, wd=P, yp=P, ws=P,
-        nbytes=1 << 30):
+def ffn(n_max=1000, d=128, E=4, F=128, dt=1, xp=P, n_in=0, rows=None, off=P, wg=P, wu=P, wd=P, yp=P, gu=None,
+        ws=P, nbytes=1 << 30):
     n = ctypes.c_size_t(nbytes)
-    return B.lib().moe_grouped_ffn(n_max, d, E, F, dt, xp, n_in, rows, off, wg, wu, wd, yp, ws, ctypes.byref(n),
-                                   None)
+    return B.lib().moe_grouped_ffn(n_max, d, E, F, dt, xp, n_in, rows, off, wg, wu, wd, yp, gu, ws,
+                                   ctypes.byref(n), None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(n_max=0), INVALID), (dict(F=0), INVALID), (dict(F=100), UNSUPPORTED), (dict(d=65), UNSUPPORTED),
     (dict(E=2000), UNSUPPORTED), (dict(n_max=1 << 31), UNSUPPORTED),
     (dict(xp=None), INVALID), (dict(off=None), INVALID), (dict(wg=None), INVALID), (dict(wu=P_MIS), INVALID),
-    (dict(wd=None), INVALID), (dict(yp=P_MIS), INVALID), (dict(nbytes=1000 * 128 * 2 - 1), WORKSPACE),
+    (dict(wd=None), INVALID), (dict(yp=P_MIS), INVALID), (dict(gu=P_MIS), INVALID),
+    (dict(nbytes=1000 * 128 * 2 - 1), WORKSPACE),
     # in-place gather: n_in rows of x, 32-bit byte offsets
     (dict(rows=P, n_in=0), INVALID), (dict(rows=P, n_in=(1 << 31) // 128), UNSUPPORTED),
     (dict(rows=ctypes.c_void_p(0x10001), n_in=100), INVALID),
@@ -162,15 +169,15 @@ def test_combine_argument_errors(args, status):
 
 
 def layer(T=64, d=128, E=8, k=2, F=128, dt=1, x=P, wr=P, b=None, wg=P, wu=P, wd=P, y=P, logits=None, ids=None,
-          w=None, off=None, ws=P, nbytes=1 << 30):
+          w=None, off=None, yp=None, gu=None, ws=P, nbytes=1 << 30):
     n = ctypes.c_size_t(nbytes)
-    return B.lib().moe_layer_forward(T, d, E, k, F, dt, x, wr, b, wg, wu, wd, y, logits, ids, w, off, ws,
+    return B.lib().moe_layer_forward(T, d, E, k, F, dt, x, wr, b, wg, wu, wd, y, logits, ids, w, off, yp, gu, ws,
                                      ctypes.byref(n), None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(F=0), INVALID), (dict(F=96), UNSUPPORTED), (dict(k=9), INVALID), (dict(y=None), INVALID),
-    (dict(wg=P_MIS), INVALID),
+    (dict(wg=P_MIS), INVALID), (dict(yp=P_MIS), INVALID), (dict(gu=P_MIS), INVALID),
     # pre-routed: ids and weights are required inputs, bias and logits not allowed
     (dict(wr=None), INVALID), (dict(wr=None, ids=P), INVALID), (dict(wr=None, ids=P, w=P, b=P), INVALID),
     (dict(wr=None, ids=P, w=P, logits=P), INVALID),
@@ -221,28 +228,30 @@ def test_newton_schulz_argument_errors(kw, status):
 
 # ---- expert-FFN backward --------------------------------------------------------
 
-def bwd_ws(n_max, d, E, F, es=2):
+def bwd_ws(n_max, d, E, F, es=2, saved=False):
     n_pad = (n_max + 63 * E + 63) // 64 * 64
     # transposed weight copies only for float32 layers (16-bit weights are read in place)
     wcopies = ru(E * F * d * es) + ru(E * d * 2 * F * es) if es == 4 else 0
     # sanitised offsets, padded offsets, block owners
-    return (2 * ru((E + 1) * 4) + ru(n_pad // 64 * 4) + wcopies + ru(n_max * F * 4)
+    # (no float32 dH when the forward's G | U are given)
+    return (2 * ru((E + 1) * 4) + ru(n_pad // 64 * 4) + wcopies + (0 if saved else ru(n_max * F * 4))
             + ru(n_max * 2 * F * es) + ru(n_max * F * es) + 2 * ru(d * n_pad * es) + 3 * ru(F * n_pad * es))
 
 
 @pytest.mark.parametrize("n_max,d,E,F,dt", [(1000, 128, 4, 192, 1), (524288, 6144, 384, 1792, 1), (64, 64, 1, 64, 1),
                                             (512, 128, 16, 64, 0)])
 def test_ffn_backward_workspace_query(n_max, d, E, F, dt):
-    nb = ctypes.c_size_t(12345)
-    st = B.lib().moe_grouped_ffn_backward(n_max, d, E, F, dt, P, 0, None, P, P, P, P, P, P, P, P, P, None,
-                                          ctypes.byref(nb), None)
-    assert st == OK and nb.value == bwd_ws(n_max, d, E, F, 2 if dt == 1 else 4)
+    for saved in (False, True):
+        nb = ctypes.c_size_t(12345)
+        st = B.lib().moe_grouped_ffn_backward(n_max, d, E, F, dt, P, 0, None, P, P, P, P, P, P if saved else None, P,
+                                              P, P, P, None, ctypes.byref(nb), None)
+        assert st == OK and nb.value == bwd_ws(n_max, d, E, F, 2 if dt == 1 else 4, saved)
 
 
-def bwd(n_max=1000, d=128, E=4, F=128, dt=1, xp=P, n_in=0, rows=None, off=P, wg=P, wu=P, wd=P, dy=P, dx=P,
-        dwg=P, dwu=P, dwd=P, ws=P, nbytes=1 << 36):
+def bwd(n_max=1000, d=128, E=4, F=128, dt=1, xp=P, n_in=0, rows=None, off=P, wg=P, wu=P, wd=P, dy=P, gu=None,
+        dx=P, dwg=P, dwu=P, dwd=P, ws=P, nbytes=1 << 36):
     nb = ctypes.c_size_t(nbytes)
-    return B.lib().moe_grouped_ffn_backward(n_max, d, E, F, dt, xp, n_in, rows, off, wg, wu, wd, dy, dx, dwg,
+    return B.lib().moe_grouped_ffn_backward(n_max, d, E, F, dt, xp, n_in, rows, off, wg, wu, wd, dy, gu, dx, dwg,
                                             dwu, dwd, ws, ctypes.byref(nb), None)
 
 
@@ -250,7 +259,8 @@ def bwd(n_max=1000, d=128, E=4, F=128, dt=1, xp=P, n_in=0, rows=None, off=P, wg=
     (dict(n_max=0), INVALID), (dict(F=0), INVALID), (dict(F=100), UNSUPPORTED), (dict(d=65), UNSUPPORTED),
     (dict(E=2000), UNSUPPORTED), (dict(dt=9), UNSUPPORTED),
     (dict(xp=None), INVALID), (dict(off=None), INVALID), (dict(dy=P_MIS), INVALID), (dict(dx=None), INVALID),
-    (dict(dwg=P_MIS), INVALID), (dict(dwd=None), INVALID), (dict(nbytes=1000), WORKSPACE),
+    (dict(dwg=P_MIS), INVALID), (dict(dwd=None), INVALID), (dict(gu=P_MIS), INVALID),
+    (dict(nbytes=1000), WORKSPACE),
     (dict(rows=P, n_in=0), INVALID), (dict(rows=P, n_in=(1 << 31) // 128), UNSUPPORTED),
     (dict(rows=ctypes.c_void_p(0x10001), n_in=100), INVALID),
 ])
@@ -318,14 +328,14 @@ def test_route_backward_argument_errors(kw, status):
     assert rbwd(**kw) == status
 
 
-def layer_bwd_ws(T, d, E, k, F, es, routed=True, g_given=False):
+def layer_bwd_ws(T, d, E, k, F, es, routed=True, g_given=False, saved=False):
     slots = T * k
     n = ru((E + 1) * 4) + 2 * ru(slots * 4) + ru(-(-T // 256) * E * 4)
     n += 0 if g_given else ru(slots * 4)
     n += 2 * ru(slots * d * es)
     if T * d * es >= 1 << 32:
         n += ru(slots * d * es)
-    n += bwd_ws(slots, d, E, F, es)
+    n += bwd_ws(slots, d, E, F, es, saved)
     return n + (route_bwd_ws(T, d, E, es) if routed else 0)
 
 
@@ -336,25 +346,26 @@ def test_layer_backward_workspace_query(T, d, E, k, F, dt):
     es = 2 if dt == 1 else 4
     for routed in (True, False):
         for g_given in (False, True):
-            nb = ctypes.c_size_t(12345)
-            st = B.lib().moe_layer_backward(T, d, E, k, F, dt, P, P if routed else None, P, P, P, P, P, P, P, P,
-                                            P if routed else None, None, P, P, P, P if g_given else None, None,
-                                            ctypes.byref(nb), None)
-            assert st == OK and nb.value == layer_bwd_ws(T, d, E, k, F, es, routed, g_given)
+            for saved in (False, True):
+                nb = ctypes.c_size_t(12345)
+                st = B.lib().moe_layer_backward(T, d, E, k, F, dt, P, P if routed else None, P, P, P, P, P, P,
+                                                P if saved else None, P, P, P if routed else None, None, P, P, P,
+                                                P if g_given else None, None, ctypes.byref(nb), None)
+                assert st == OK and nb.value == layer_bwd_ws(T, d, E, k, F, es, routed, g_given, saved)
 
 
-def lbwd(T=64, d=128, E=8, k=2, F=128, dt=1, x=P, wr=P, wg=P, wu=P, wd=P, ids=P, w=P, yp=P, dy=P, dx=P, dwr=P,
-         db=None, dwg=P, dwu=P, dwd=P, g=None, ws=P, nbytes=1 << 34):
+def lbwd(T=64, d=128, E=8, k=2, F=128, dt=1, x=P, wr=P, wg=P, wu=P, wd=P, ids=P, w=P, yp=P, gu=None, dy=P, dx=P,
+         dwr=P, db=None, dwg=P, dwu=P, dwd=P, g=None, ws=P, nbytes=1 << 34):
     nb = ctypes.c_size_t(nbytes)
-    return B.lib().moe_layer_backward(T, d, E, k, F, dt, x, wr, wg, wu, wd, ids, w, yp, dy, dx, dwr, db, dwg, dwu,
-                                      dwd, g, ws, ctypes.byref(nb), None)
+    return B.lib().moe_layer_backward(T, d, E, k, F, dt, x, wr, wg, wu, wd, ids, w, yp, gu, dy, dx, dwr, db, dwg,
+                                      dwu, dwd, g, ws, ctypes.byref(nb), None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(T=0), INVALID), (dict(F=0), INVALID), (dict(F=96), UNSUPPORTED), (dict(k=9), INVALID),
     (dict(d=65), UNSUPPORTED), (dict(dt=2), UNSUPPORTED), (dict(yp=None), INVALID), (dict(dy=P_MIS), INVALID),
     (dict(dx=None), INVALID), (dict(dwg=None), INVALID), (dict(ids=None), INVALID), (dict(w=P_MIS), INVALID),
-    (dict(dwr=None), INVALID), (dict(g=P_MIS), INVALID),
+    (dict(dwr=None), INVALID), (dict(g=P_MIS), INVALID), (dict(gu=P_MIS), INVALID),
     # pre-routed: no router gradients may be asked for
     (dict(wr=None), INVALID), (dict(wr=None, dwr=None, db=P), INVALID),
     (dict(nbytes=1000), WORKSPACE), (dict(ws=ctypes.c_void_p(0x10010)), INVALID),

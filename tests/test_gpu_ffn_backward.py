@@ -132,3 +132,94 @@ def test_ffn_backward_page_shape_largest_expert_in_full():
         close_scaled(f64(dwu[e]), ref[2], f"dW_up[{e}]")
         close_scaled(f64(dwd[e]), ref[3], f"dW_down[{e}]")
         del ref
+
+
+# ---------------------------------------------------------------------------
+# the forward keeps G | U; the backward reads them instead of recomputing
+# ---------------------------------------------------------------------------
+
+def gate_up_bound(X, W, o):
+    """Bound on a kept pre-activation: a float32 sum over K = d exact products of
+    bf16 values (error <= K 2^-24 sum |x w|), then one rounding to bf16 (relative
+    2^-8 at most)."""
+    acc = X.shape[1] * 2.0 ** -24 * (np.abs(X) @ np.abs(W).T)
+    return 2.0 ** -8 * (np.abs(o) + acc) + acc
+
+
+@pytest.mark.parametrize("counts,d,F,gather", CASES[:4] + CASES[5:6])
+def test_forward_keeps_gate_up_pre_activations(counts, d, F, gather):
+    print(f"[gu] counts={counts} d={d} F={F} gather={gather}", flush=True)
+    off, x_in, rows, xp, wg, wu, wd, dy = make(counts, d, F, seed=sum(counts) + 2 * d + F, gather=gather)
+    n_max = dy.shape[0]
+    gu = torch.full((n_max, 2 * F), 7.0, dtype=torch.bfloat16, device=DEV)
+    y0 = B.moe_grouped_ffn(x_in, off, wg, wu, wd, a_rows=rows, n_max=n_max)
+    y1 = B.moe_grouped_ffn(x_in, off, wg, wu, wd, a_rows=rows, n_max=n_max, gu_out=gu)
+    torch.cuda.synchronize()
+    n = int(off[-1])
+    assert torch.equal(y0[:n].view(torch.int16), y1[:n].view(torch.int16))   # y_perm unchanged
+    assert (gu[n:] == 7.0).all()                                             # rows past offsets[E] untouched
+    offs = off.cpu().numpy().astype(np.int64)
+    for e in range(len(counts)):
+        lo, hi = offs[e], offs[e + 1]
+        if hi == lo:
+            continue
+        X = f64(xp[lo:hi])
+        for half, Wt in ((0, wg[e]), (1, wu[e])):
+            o = X @ f64(Wt).T
+            got = f64(gu[lo:hi, half * F:(half + 1) * F])
+            assert (np.abs(got - o) <= gate_up_bound(X, f64(Wt), o)).all(), (e, half, np.abs(got - o).max())
+
+
+@pytest.mark.parametrize("counts,d,F,gather", CASES)
+def test_ffn_backward_from_kept_gate_up_matches_oracle(counts, d, F, gather):
+    # G and U rounded to bf16 once more than on the recompute path: within the same rule
+    print(f"[bwd-gu] counts={counts} d={d} F={F} gather={gather}", flush=True)
+    off, x_in, rows, xp, wg, wu, wd, dy = make(counts, d, F, seed=sum(counts) + d + F, gather=gather)
+    n_max = dy.shape[0]
+    gu = torch.empty(n_max, 2 * F, dtype=torch.bfloat16, device=DEV)
+    B.moe_grouped_ffn(x_in, off, wg, wu, wd, a_rows=rows, n_max=n_max, gu_out=gu)
+    dx, dwg, dwu, dwd = B.moe_grouped_ffn_backward(x_in, off, wg, wu, wd, dy, a_rows=rows, gu=gu)
+    torch.cuda.synchronize()
+    n = int(off[-1])
+    ref = bo.grouped_ffn_backward(f64(xp[:n]), off.cpu().numpy(), f64(wg), f64(wu), f64(wd), f64(dy[:n]))
+    close_scaled(f64(dx[:n]), ref[0], "dx")
+    for e, c in enumerate(counts):
+        for got, want, nm in ((dwg, ref[1], "dW_gate"), (dwu, ref[2], "dW_up"), (dwd, ref[3], "dW_down")):
+            if c == 0:
+                assert not got[e].any(), (nm, e)
+            else:
+                close_scaled(f64(got[e]), want[e], f"{nm}[{e}]")
+
+
+def test_ffn_backward_page_shape_from_kept_gate_up():
+    # the page-shape workload through the kept-G|U path: every dX row and all three
+    # weight gradients of the largest expert, plus its kept G | U rows
+    wl = W.WORKLOADS["page_seq64k_skewed"]
+    print(f"[bwd-gu] page shape T={wl.T} d={wl.d} E={wl.E} F={wl.F}", flush=True)
+    inp = W.make_inputs(wl, device=DEV)
+    ids, w, _ = B.moe_route(inp["x"], inp["w_router"], wl.k, bias=inp["bias"], want_logits=False)
+    off, rt, sr, _ = B.moe_permute(inp["x"], ids, wl.E, copy_rows=False)
+    n_max = rt.numel()
+    gu = torch.empty(n_max, 2 * wl.F, dtype=torch.bfloat16, device=DEV)
+    B.moe_grouped_ffn(inp["x"], off, inp["w_gate"], inp["w_up"], inp["w_down"], a_rows=rt, n_max=n_max, gu_out=gu)
+    g = torch.Generator(device=DEV).manual_seed(12)
+    dy = torch.randn(n_max, wl.d, generator=g, device=DEV).to(torch.bfloat16)
+    dx, dwg, dwu, dwd = B.moe_grouped_ffn_backward(inp["x"], off, inp["w_gate"], inp["w_up"], inp["w_down"], dy,
+                                                   a_rows=rt, gu=gu)
+    torch.cuda.synchronize()
+    offs = off.cpu().numpy().astype(np.int64)
+    e = int(np.argmax(np.diff(offs)))
+    lo, hi = offs[e], offs[e + 1]
+    print(f"[bwd-gu] expert {e}: {hi - lo} rows in full", flush=True)
+    idx = torch.arange(lo, hi, device=DEV)
+    X = f64(inp["x"][rt[idx].long()])
+    for half, Wt in ((0, inp["w_gate"][e]), (1, inp["w_up"][e])):
+        o = X @ f64(Wt).T
+        got = f64(gu[idx, half * wl.F:(half + 1) * wl.F])
+        assert (np.abs(got - o) <= gate_up_bound(X, f64(Wt), o)).all(), (half, np.abs(got - o).max())
+        del o, got
+    ref = bo.expert_ffn_backward(X, f64(inp["w_gate"][e]), f64(inp["w_up"][e]), f64(inp["w_down"][e]), f64(dy[idx]))
+    close_scaled(f64(dx[idx]), ref[0], f"dX, every row of expert {e}")
+    close_scaled(f64(dwg[e]), ref[1], f"dW_gate[{e}]")
+    close_scaled(f64(dwu[e]), ref[2], f"dW_up[{e}]")
+    close_scaled(f64(dwd[e]), ref[3], f"dW_down[{e}]")

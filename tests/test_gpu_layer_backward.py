@@ -224,3 +224,47 @@ def test_route_backward_page_shape_sampled():
     dx_perm_part = lbo.permute_backward(f64(dxp[torch.from_numpy(rows.astype(np.int64)).to(DEV)]), sub_rt, S.size)
     dx_router_part = ref_dl[S] @ f64(wr)
     close_bf16(f64(dx[St]), dx_perm_part + dx_router_part, "dx (sampled tokens)")
+
+
+@pytest.mark.parametrize("T,d,E,k,F,dtype,seed,bias", LAYERS)
+def test_layer_backward_from_kept_gate_up(T, d, E, k, F, dtype, seed, bias):
+    # The forward (fed the oracle's routing, so no oracle input comes from the GPU)
+    # keeps G | U; the backward reads them.  bf16: G and U are rounded once more than
+    # on the recompute path, within the same rule.  float32: the kept values are the
+    # recompute path's accumulators, so every output equals that path's bit for bit.
+    print(f"[lbwd-gu] T={T} d={d} E={E} k={k} F={F} {dtype}", flush=True)
+    gpu, ref = small_layer(T, d, E, k, F, dtype, seed, bias)
+    inp = gpu["inp"]
+    Lf = B.moe_layer_forward(inp["x"], None, None, inp["w_gate"], inp["w_up"], inp["w_down"], k,
+                             topk_ids=gpu["ids"], topk_w=gpu["w"], want_y_perm=True, want_gu=True)
+    L = B.moe_layer_backward(inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"], gpu["ids"],
+                             gpu["w"], gpu["y_perm"], gpu["dy"], want_bias=True, want_d_topk_w=True, gu=Lf.gu)
+    torch.cuda.synchronize()
+    check_layer(L, ref, dtype)
+    if dtype == torch.float32:
+        R = run_layer(gpu)
+        torch.cuda.synchronize()
+        for a, b in ((L.dx, R.dx), (L.dw_gate, R.dw_gate), (L.dw_up, R.dw_up), (L.dw_down, R.dw_down),
+                     (L.dw_router, R.dw_router), (L.dbias, R.dbias), (L.d_topk_w, R.d_topk_w)):
+            assert torch.equal(a, b)
+
+
+def test_layer_forward_training_outputs():
+    # y_perm_out and gu_out change nothing in y; y_perm_out is the stage path's y_perm
+    T, d, E, k, F = 300, 256, 12, 4, 128
+    print("[lbwd-gu] forward outputs for training", flush=True)
+    wl = W.Workload("train_fwd", T, d, E, k, F, torch.bfloat16, routing="router_bias", seed=6)
+    inp = W.make_inputs(wl, device=DEV)
+    a = B.moe_layer_forward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"], inp["w_down"], k,
+                            want_routing=True, want_offsets=True)
+    b = B.moe_layer_forward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"], inp["w_down"], k,
+                            want_routing=True, want_offsets=True, want_y_perm=True, want_gu=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.y.view(torch.int16), b.y.view(torch.int16))
+    off, rt, sr, _ = B.moe_permute(inp["x"], b.topk_ids, E, copy_rows=False)
+    gu = torch.empty(T * k, 2 * F, dtype=torch.bfloat16, device=DEV)
+    yp = B.moe_grouped_ffn(inp["x"], off, inp["w_gate"], inp["w_up"], inp["w_down"], a_rows=rt, gu_out=gu)
+    torch.cuda.synchronize()
+    n = int(off[-1])
+    assert torch.equal(yp[:n].view(torch.int16), b.y_perm[:n].view(torch.int16))
+    assert torch.equal(gu[:n].view(torch.int16), b.gu[:n].view(torch.int16))

@@ -37,7 +37,7 @@ def _noalloc(inp, wl, routed):
         ids, w, logits = inp["topk_ids"], inp["topk_w"], None
     st = _fn()(T, d, E, k, F, B.dtype_code(wl.dtype), _p(inp["x"]), _p(inp["w_router"]), _p(inp["bias"]),
                _p(inp["w_gate"]), _p(inp["w_up"]), _p(inp["w_down"]), _p(y), _p(logits), _p(ids), _p(w), _p(off),
-               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+               None, None, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     assert st == 0, st
     return y, logits, ids, w, off
 
@@ -78,5 +78,5 @@ def test_noalloc_pre_routed_and_fp32():
 def test_noalloc_refuses_more_than_its_array():
     # the page's layer shape at 65,536 tokens needs about 8.3 GB: refused on the host
     P = ctypes.c_void_p(0x10000)
-    st = _fn()(65536, 6144, 384, 8, 1792, 1, P, P, None, P, P, P, P, None, None, None, None, None)
+    st = _fn()(65536, 6144, 384, 8, 1792, 1, P, P, None, P, P, P, P, None, None, None, None, None, None, None)
     assert st == 3
