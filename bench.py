@@ -82,7 +82,7 @@ def parse():
 # of the page shape, from rocprofv3 FETCH_SIZE and WRITE_SIZE runs of
 # `bench.py --traffic-probe`, each scaled by the same counter's reading for a
 # 1 GiB device copy.  Valid only for the kernel sources it was measured on.
-TRAFFIC = {"workload": "page_seq64k_skewed", "kernel_source_hash": "771078bf4984293f", "bytes": 101200381364,
+TRAFFIC = {"workload": "page_seq64k_skewed", "kernel_source_hash": "f7fafd382b194657", "bytes": 99547995081,
            "fetch_scale": 1.9999, "write_scale": 1.0000}
 KERNEL_SOURCES = ["mixture_experts_layer_16_amd/csrc/gemm_tile.h", "mixture_experts_layer_16_amd/csrc/grouped_ffn.hip",
                   "mixture_experts_layer_16_amd/csrc/common.h", "mixture_experts_layer_16_amd/csrc/tile_walk.h"]
