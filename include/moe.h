@@ -211,7 +211,8 @@ moe_status moe_layer_forward(int64_t T, int64_t d, int64_t E, int64_t k, int64_t
  * the library runs on holds until the process ends; a call whose workspace query
  * (moe_layer_forward with ws == NULL) exceeds it returns MOE_ERR_WORKSPACE before
  * anything is launched.  At the page's layer shape (d 6,144, E 384, top-8, F
- * 1,792, bf16) that is up to 521 routed tokens per call.  Same kernels and results as
+ * 1,792, bf16) that is up to 521 routed tokens per call (2,211 with y_perm_out
+ * given, which takes y_perm out of the workspace).  Same kernels and results as
  * moe_layer_forward; it calls no allocator.  Calls that overlap on one GPU share
  * the array and race: order them on one stream (or synchronise between them).
  * Arguments and errors as moe_layer_forward.
