@@ -78,6 +78,37 @@ def test_layer_backward_graph_replays_match_eager():
     replay_and_check(g, outs, expected, lambda: junk.mul_(1.0001))
 
 
+def test_training_step_graph_replays_match_eager():
+    # one training step's layer work in one graph: the forward keeping y_perm and
+    # G | U, then the backward reading them
+    print("[graph] forward keeping G|U + backward from it", flush=True)
+    T, d, E, k, F = 900, 256, 16, 4, 192
+    wl = W.Workload("graph_train", T, d, E, k, F, torch.bfloat16, routing="router_bias", seed=2)
+    inp = W.make_inputs(wl, device=DEV)
+    LF = B.LayerForward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"], inp["w_down"], k,
+                        want_routing=True, want_y_perm=True, want_gu=True)
+    LF()
+    torch.cuda.synchronize()
+    dy = W.output_grad(T, d, torch.bfloat16, DEV, seed=5)
+    LB = B.LayerBackward(inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"], LF.topk_ids,
+                         LF.topk_w, LF.y_perm, dy, want_d_topk_w=True, gu=LF.gu)
+    LB()
+    torch.cuda.synchronize()
+    outs = [LF.y, LF.topk_ids, LF.topk_w, LB.dx, LB.dw_router, LB.dbias, LB.dw_gate, LB.dw_up, LB.dw_down,
+            LB.d_topk_w]
+    expected = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            LF()
+            LB()
+    torch.cuda.current_stream().wait_stream(s)
+    junk = torch.randn(1 << 20, device=DEV)
+    replay_and_check(g, outs, expected, lambda: junk.mul_(1.0001))
+
+
 def test_newton_schulz_graph_replays_match_eager():
     print("[graph] newton-schulz", flush=True)
     gen = torch.Generator(device=DEV).manual_seed(4)
