@@ -656,6 +656,16 @@ def main():
         "route": route,
         "kernels": kernels,
     }
+    # the same forward for training: y_perm and the gate/up pre-activations G | U
+    # written to the caller's buffers for the backward
+    LT = B.LayerForward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"], inp["w_down"], wl.k,
+                        topk_ids=inp.get("topk_ids"), topk_w=inp.get("topk_w"), want_y_perm=True, want_gu=True)
+    LT()
+    ms_train = time_layer(torch, LT, max(2, min(args.steps, 5)))
+    out["training_forward"] = {"ms_per_step": round(ms_train, 4), "tokens_per_s": round(wl.T / (ms_train / 1e3), 1),
+                               "note": "moe_layer_forward also writing y_perm and G | U for the backward"}
+    del LT
+    torch.cuda.empty_cache()
     if args.cpu_tokens > 0:
         out["cpu_baseline"] = cpu_baseline(torch, inp, wl, args.cpu_tokens)
     del L, inp
