@@ -138,6 +138,14 @@ def test_layer_backward_pre_routed():
     torch.cuda.synchronize()
     check_layer(L, ref, torch.bfloat16, routed=False)
     assert not L.d_topk_w[torch.from_numpy(ids < 0).to(DEV)].any()
+    # the same share from the gate/up pre-activations its forward kept
+    Lf = B.moe_layer_forward(inp["x"], None, None, inp["w_gate"], inp["w_up"], inp["w_down"], k,
+                             topk_ids=inp["topk_ids"], topk_w=inp["topk_w"], want_gu=True)
+    K = B.moe_layer_backward(inp["x"], None, inp["w_gate"], inp["w_up"], inp["w_down"], inp["topk_ids"],
+                             inp["topk_w"], y_perm, dy, want_bias=False, want_d_topk_w=True, gu=Lf.gu)
+    torch.cuda.synchronize()
+    check_layer(K, ref, torch.bfloat16, routed=False)
+    assert torch.equal(K.d_topk_w, L.d_topk_w)          # the combine backward does not see G | U
 
 
 def test_layer_backward_is_deterministic_and_equals_its_steps():
