@@ -4,7 +4,7 @@ configuration that bench.py times (moe_layer_forward).  The oracle checks:
     oracle selects on the GPU's logits; the logits themselves on a token sample;
   * the expert offsets, bit-exact;
   * the grouped FFN (stage entry points) on EVERY row of the largest expert's
-    first two chunks of 8 row tiles and of its last chunk (the tile order walks
+    first four chunks of 8 row tiles and of its last chunk (the tile order walks
     a large expert chunk by chunk), and on sampled rows of the smallest non-empty
     expert and two random ones;
   * the layer output on 256 sampled tokens (plus a token with no local slot);
@@ -95,11 +95,11 @@ def test_full_size_sampled_parity(name):
         ref = orc.expert_ffn(X, *expert_f64(inp, e))
         assert_close(f64(yp[idx]), ref, wl.dtype, what)
 
-    # every row of the largest expert's first two chunks and of its last chunk
+    # every row of the largest expert's first four chunks and of its last chunk
     big = int(np.argmax(counts))
     lo, hi = int(r_off[big]), int(r_off[big + 1])
     last = lo + (hi - lo - 1) // ROW_CHUNK * ROW_CHUNK
-    rows = np.unique(np.concatenate([np.arange(lo, min(hi, lo + 2 * ROW_CHUNK)), np.arange(last, hi)]))
+    rows = np.unique(np.concatenate([np.arange(lo, min(hi, lo + 4 * ROW_CHUNK)), np.arange(last, hi)]))
     print(f"[full-size] {name}: expert {big} ({hi - lo} rows): {rows.size} rows compared", flush=True)
     check_rows(big, rows, f"y_perm rows of expert {big}")
     # sampled rows of the smallest non-empty expert and two random ones
