@@ -107,7 +107,8 @@ static std::vector<int32_t> offsets_of(const std::vector<int>& counts) {
 int main() {
   std::vector<Case> cases;
   // the forward's launch shapes: 256-row tiles, gate/up 128 output columns per
-  // tile (F = 384 -> 3), down 256 (d = 768 -> 3); 16 x 2 chunks
+  // tile (F = 384 -> 3), down 256 (d = 768 -> 3); 16 x 2 chunks (8 x 2, the
+  // forward's current order, below)
   auto fwd = [&](const char* n, std::vector<int> counts, int N, int NOUT) {
     const auto o = offsets_of(counts);
     cases.push_back({n, o, (int64_t)o.back() + 37, 256, N, NOUT, 16, 2, true, INT64_MAX});
@@ -117,6 +118,14 @@ int main() {
   fwd("one long expert", {5000, 0, 3}, 192, 128);
   fwd("exact chunks", {8192, 4096, 0, 1}, 1792, 128);
   fwd("page shape skew", {27781, 226, 5000, 0, 4097, 4095, 4096}, 6144, 256);
+  // the forward's chunks of 8 row tiles (the ones above use 16)
+  auto fwd8 = [&](const char* n, std::vector<int> counts, int N, int NOUT) {
+    const auto o = offsets_of(counts);
+    cases.push_back({n, o, (int64_t)o.back() + 37, 256, N, NOUT, 8, 2, true, INT64_MAX});
+  };
+  fwd8("ragged gate/up, chunks of 8", {4400, 0, 300, 37}, 384, 128);
+  fwd8("page shape skew, chunks of 8", {27781, 226, 5000, 0, 4097, 4095, 4096}, 1792, 128);
+  fwd8("one long expert, chunks of 8", {5000, 0, 3}, 6144, 256);
   std::mt19937 rng(1);
   for (int r = 0; r < 20; ++r) {
     std::vector<int> counts(1 + rng() % 60);
@@ -133,7 +142,7 @@ int main() {
                    16, 2, false, 200000});
   {
     std::vector<int32_t> seg(1025);
-    for (auto& v : seg) v = (int32_t)(rng() % 4000000000u) - 2000000000;
+    for (auto& v : seg) v = (int32_t)((int64_t)(rng() % 4000000000u) - 2000000000);
     cases.push_back({"random garbage 1024", seg, 2000000000, 256, 8192, 128, 16, 2, false, 200000});
   }
   for (const auto& c : cases) run(c);
